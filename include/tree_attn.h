@@ -1,0 +1,210 @@
+/*
+ * tree_attn.h - attention over prefix-tree-packed rows on AMD Instinct MI355X (gfx950).
+ *
+ * A batch of token sequences that share prefixes is packed as a trie: a
+ * shared prefix is stored once, laid out depth-first, each token takes its
+ * tree depth as position id, and each token attends only to itself and its
+ * root-to-leaf ancestors.  This library is the data-parallel hot path of
+ * that method, as a plain C ABI:
+ *
+ *   tree_build_trie      token sequences -> token-level parent array (host)
+ *   tree_pack_layout     parent array -> DFS slots, depth, subtree end, token_index (host)
+ *   tree_rope            rotary embedding at depth, in place (device)
+ *   tree_attn_fwd        masked attention forward (device)
+ *   tree_attn_bwd        its exact gradient (device)
+ *
+ * Sources (web pages, cited by title and section):
+ *   [ART] "Prefix Tree Packing in ART" (FurtherAI blog)
+ *   [DAG] "DAG packing" (sudakov.site)
+ *   [TRL] "TRL Tree Packing for AsyncGRPO: The 26x Claim vs. the 3x the Pull
+ *         Request Measures" (explainx.ai)
+ *
+ * Conventions shared by every entry point
+ *   - Every call returns a tree_status; TREE_OK (0) on success.  On failure
+ *     tree_last_error() returns a thread-local message naming the problem.
+ *   - Argument checks run before any device work: a call that fails them
+ *     enqueues nothing.  A failed kernel launch returns TREE_ERR_DEVICE.
+ *   - The caller owns and allocates every buffer.  Host entry points take
+ *     host pointers; device entry points take device pointers and enqueue
+ *     asynchronously on `stream` (a hipStream_t; NULL = the default stream).
+ *     The library keeps no state between calls and is thread-safe.
+ *   - Device tensors are contiguous:
+ *       q, out, dout, dq : [B, N, Hq, D]      k, v, dk, dv : [B, N, Hkv, D]
+ *       lse              : [B, Hq, N] fp32, natural log
+ *       subtree_end, pos_ids : [B, N] int32
+ *     Query head h reads KV head h / (Hq / Hkv).  D is 64 or 128.
+ *   - Integers are int32 for token ids, node ids and slots, int64 for CSR
+ *     offsets into flattened arrays.
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tree_status {
+    TREE_OK = 0,
+    TREE_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size, bad dtype */
+    TREE_ERR_BAD_TREE = 2,    /* parent array is not a forest; subtree_end not nested */
+    TREE_ERR_CAPACITY = 3,    /* an output buffer is too small (required size still reported) */
+    TREE_ERR_UNSUPPORTED = 4, /* head dim, head ratio or dtype this build has no kernel for */
+    TREE_ERR_DEVICE = 5       /* a HIP call or kernel launch failed */
+} tree_status;
+
+typedef enum tree_dtype { TREE_F32 = 0, TREE_BF16 = 1 } tree_dtype;
+
+/* Version of this ABI (bumped on any signature change). */
+int tree_abi_version(void);
+/* Static name of a status code. */
+const char* tree_status_string(int status);
+/* Message for the last failed call on this thread ("" if none). */
+const char* tree_last_error(void);
+
+/*
+ * tree_build_trie - pack token sequences into a token-level trie (host, synchronous).
+ *
+ * [ART "The tree"]: take the longest run that every active sequence agrees
+ * on, emit it once, split the rest by their next token and recurse.  A run
+ * shorter than `min_shared` tokens is not shared but copied into each
+ * next-token branch (sharing resumes deeper where a branch agrees longer).
+ * At every fork each branch keeps its own copy of the join token, the last
+ * shared token [ART "The tree"; DAG "The walk"].  The run length compared
+ * with `min_shared` is measured before the join token is split off.
+ * Branches are taken in ascending next-token order; sequences that end where
+ * the others fork come first; identical sequences share one path.  Nodes are
+ * numbered in emission order, a depth-first pre-order, so
+ * tree_pack_layout() of the result keeps node i in slot i.
+ *
+ *   n_seqs       number of sequences (>= 0)
+ *   seq_offsets  [n_seqs + 1] CSR offsets into `tokens`, non-decreasing, seq_offsets[0] == 0
+ *   tokens       [seq_offsets[n_seqs]] token ids (any int32 values)
+ *   min_shared   minimum shared run length (>= 1; 64 is the pages' default)
+ *   parent       out [parent_cap] parent node of each node, -1 for a root; NULL = size query
+ *   parent_cap   capacity of `parent` in elements; seq_offsets[n_seqs] always suffices
+ *   n_nodes      out: number of nodes (written also on TREE_ERR_CAPACITY)
+ *   seq_last     out [n_seqs] node of each sequence's last token, -1 for an empty sequence;
+ *                may be NULL
+ */
+tree_status tree_build_trie(int32_t n_seqs, const int64_t* seq_offsets, const int32_t* tokens,
+                            int32_t min_shared, int32_t* parent, int64_t parent_cap,
+                            int64_t* n_nodes, int32_t* seq_last);
+
+/*
+ * tree_pack_layout - lay one packed row out depth-first (host, synchronous).
+ *
+ * [TRL "How tree packing works"]: the collator lays tokens out depth-first,
+ * uses depth as position ids and keeps a token_index from each trained token
+ * back to its packed slot.  [DAG "Positions"]: depth is the number of steps
+ * from the root (roots are at depth 0).  [ART "Token-mixing layers"]: the
+ * pre-order/exit-order interval decides ancestry; subtree_end[j] is the
+ * exit half: slot j is an ancestor-or-self of slot i iff
+ * j <= i <= subtree_end[j].
+ *
+ *   n_nodes      nodes in the row's forest (0 <= n_nodes <= row_len)
+ *   parent       [n_nodes] parent node id, -1 for a root; any numbering
+ *   n_seqs       number of sequences whose paths are wanted in token_index
+ *   seq_last     [n_seqs] node of each sequence's last token (-1: empty sequence)
+ *   row_len      slots in the row; slots >= n_nodes are padding
+ *   slot_node    out [row_len] node in each slot, -1 for padding
+ *   pos_ids      out [row_len] depth of each slot (0 for padding)
+ *   subtree_end  out [row_len] last slot of each slot's subtree (padding: its own slot)
+ *   seq_offsets  out [n_seqs + 1] CSR offsets into token_index
+ *   token_index  out [token_index_cap] slot of every token of every sequence, root first;
+ *                NULL = size query (seq_offsets is still written)
+ *
+ * Children are visited in ascending node id.  The walk is iterative (rows of
+ * tens of thousands of tokens are chains that deep).  Returns
+ * TREE_ERR_BAD_TREE for a parent out of range or a cycle, TREE_ERR_CAPACITY
+ * when token_index_cap < seq_offsets[n_seqs].
+ */
+tree_status tree_pack_layout(int32_t n_nodes, const int32_t* parent, int32_t n_seqs,
+                             const int32_t* seq_last, int32_t row_len, int32_t* slot_node,
+                             int32_t* pos_ids, int32_t* subtree_end, int64_t* seq_offsets,
+                             int32_t* token_index, int64_t token_index_cap);
+
+/*
+ * tree_validate_subtree_end - check a subtree_end row (host, synchronous).
+ * TREE_OK iff j <= subtree_end[j] < n for every j and the intervals
+ * [j, subtree_end[j]] are nested or disjoint (a valid pre-order interval
+ * set).  The device entry points trust their subtree_end; call this on
+ * input that did not come from tree_pack_layout().
+ */
+tree_status tree_validate_subtree_end(const int32_t* subtree_end, int64_t n);
+
+/*
+ * tree_rope - rotary position embedding at tree depth, in place (device).
+ *
+ * [DAG "Positions"]: positions are graph depth, so along every root-to-leaf
+ * path neighbouring tokens are one position apart.  Rotate-half pairing:
+ * dimensions i and i + D/2 rotate by pos * theta^(-2i/D), i < D/2.  Angles
+ * and sines are taken in fp64 and the result is rounded once to `dt`.
+ *
+ *   x        [B, N, H, D] of dtype dt, rotated in place
+ *   pos_ids  [B, N] int32 (tree_pack_layout's pos_ids per row)
+ *   theta    base (> 0), e.g. 10000
+ */
+tree_status tree_rope(tree_dtype dt, void* x, int64_t B, int64_t N, int64_t H, int64_t D,
+                      const int32_t* pos_ids, float theta, void* stream);
+
+/*
+ * tree_attn_workspace_bytes - device workspace tree_attn_fwd (bwd = 0) or
+ * tree_attn_bwd (bwd = 1) needs for these sizes.  Returns 0 on bad sizes.
+ */
+size_t tree_attn_workspace_bytes(tree_dtype dt, int64_t B, int64_t N, int64_t Hq, int64_t Hkv,
+                                 int64_t D, int bwd);
+
+/*
+ * tree_attn_fwd - attention forward over packed rows (device).
+ *
+ * [ART "Token-mixing layers"; DAG "The mask"]: query i attends to key j iff
+ * j is i or an ancestor of i, i.e. j <= i <= subtree_end[j].  The row's
+ * visible set splits into fully visible blocks (ancestor segments) and a
+ * causal block on its own segment; blocks with no visible pair are skipped.
+ *
+ *   out[b,i,h,:] = sum_j P[i,j] v[b,j,h/(Hq/Hkv),:],  P = softmax_j(softmax_scale * q_i . k_j)
+ *   lse[b,h,i]   = log sum_j exp(softmax_scale * q_i . k_j)     (visible j only)
+ *
+ *   dt           TREE_BF16 (MFMA, fp32 accumulation and softmax) or TREE_F32
+ *   q, k, v      inputs in dt (see layouts above); typically after tree_rope
+ *   subtree_end  [B, N] int32 from tree_pack_layout (not checked on device)
+ *   softmax_scale  usually 1/sqrt(D)
+ *   out          out [B, N, Hq, D] in dt
+ *   lse          out [B, Hq, N] fp32
+ *   ws, ws_bytes device workspace of at least tree_attn_workspace_bytes(dt, ..., 0) bytes
+ *
+ * Padding slots (subtree_end[j] == j, no descendants) attend to themselves only.
+ */
+tree_status tree_attn_fwd(tree_dtype dt, const void* q, const void* k, const void* v,
+                          const int32_t* subtree_end, int64_t B, int64_t N, int64_t Hq,
+                          int64_t Hkv, int64_t D, float softmax_scale, void* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tree_attn_bwd - exact gradient of tree_attn_fwd (device).
+ *
+ * The pages give no backward pass; this is the exact gradient of the
+ * forward above for L = sum <dout, out>, each packed slot counted once
+ * (a shared token is forwarded once, so its gradient arrives once).
+ * dk and dv sum over the query heads that share a KV head.
+ *
+ *   out, lse     the forward's outputs for these inputs
+ *   dout         [B, N, Hq, D] in dt
+ *   dq           out [B, N, Hq, D] in dt
+ *   dk, dv       out [B, N, Hkv, D] in dt
+ *   ws, ws_bytes device workspace of at least tree_attn_workspace_bytes(dt, ..., 1) bytes
+ */
+tree_status tree_attn_bwd(tree_dtype dt, const void* q, const void* k, const void* v,
+                          const int32_t* subtree_end, const void* out, const float* lse,
+                          const void* dout, int64_t B, int64_t N, int64_t Hq, int64_t Hkv,
+                          int64_t D, float softmax_scale, void* dq, void* dk, void* dv, void* ws,
+                          size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

@@ -30,6 +30,7 @@ from typing import Optional
 import numpy as np
 
 from .layout import Layout, dfs_layout
+from .precision import round_to
 from .rope import rope
 from .trie import Trie, build_trie
 
@@ -115,9 +116,9 @@ def slot_owners(token_index, n_nodes):
     return owner
 
 
-def tree_attention(sequences, fid, dkey, tables, *, theta: float, min_shared: int = 64,
+def tree_attention(sequences, fid, dkey, tables, *, theta: Optional[float], min_shared: int = 64,
                    row_len: Optional[int] = None, backward: bool = True, scale: Optional[float] = None,
-                   q_slots=None, k_slots=None) -> TreeResult:
+                   q_slots=None, k_slots=None, storage: Optional[str] = None) -> TreeResult:
     """The whole oracle path: trie, layout, RoPE at depth, per-sequence attention, map back.
 
     ``tables`` holds q [n_feat,Hq,D], k/v [n_feat,Hkv,D] and do [n_dkey,Hq,D];
@@ -125,6 +126,8 @@ def tree_attention(sequences, fid, dkey, tables, *, theta: float, min_shared: in
     By default every row of every sequence is computed.  ``q_slots`` /
     ``k_slots`` restrict the work to what out/lse/dq at ``q_slots`` and
     dk/dv at ``k_slots`` need (each of those outputs is still exact).
+    ``theta`` None applies no rotary embedding.  ``storage`` ("f32" or "bf16") rounds the rotated q and k once to the
+    dtype of the tensors that hold them; everything else stays fp64.
     """
     trie = build_trie(sequences, min_shared=min_shared)
     n = trie.n_nodes
@@ -156,8 +159,12 @@ def tree_attention(sequences, fid, dkey, tables, *, theta: float, min_shared: in
             continue
         slots = ti[s]
         pos = np.arange(L)
-        Qs = rope(qt[fid[s]], pos, theta)
-        Ks = rope(kt[fid[s]], pos, theta)
+        if theta is None:                      # no rotary embedding
+            Qs = np.asarray(qt[fid[s]], dtype=np.float64)
+            Ks = np.asarray(kt[fid[s]], dtype=np.float64)
+        else:
+            Qs = round_to(rope(qt[fid[s]], pos, theta), storage)
+            Ks = round_to(rope(kt[fid[s]], pos, theta), storage)
         Vs = np.asarray(vt[fid[s]], dtype=np.float64)
         owned = owner[slots] == s
         if sampled:

@@ -1,0 +1,22 @@
+"""Attention over prefix-tree-packed rows on AMD Instinct MI355X (gfx950).
+
+The Python names mirror the C entry points of include/tree_attn.h; all work
+happens in libtreeattn.so (host C++ for the integer layout, HIP kernels for
+everything on the device).
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    TREE_BF16,
+    TREE_F32,
+    PackedLayout,
+    TreeAttnError,
+    lib,
+    tree_attn_bwd,
+    tree_attn_fwd,
+    tree_attn_workspace_bytes,
+    tree_build_trie,
+    tree_pack_layout,
+    tree_rope,
+    tree_validate_subtree_end,
+)

@@ -1,0 +1,252 @@
+"""ctypes binding of libtreeattn.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of its own: it checks shapes and dtypes, allocates outputs when
+the caller passes none (torch for device memory, NumPy for host memory) and
+forwards raw pointers plus the current HIP stream.  If the shared library is
+missing, importing this module raises: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtreeattn.so")
+
+TREE_F32 = 0
+TREE_BF16 = 1
+
+
+class TreeAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [{status}]")
+        self.status = status
+
+
+def _load():
+    # torch ships its own HIP runtime with the same soname as ROCm's
+    # (libamdhip64.so.7).  Loading torch first makes this library bind to that
+    # one runtime, so torch's streams and allocations are valid here.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m prefix_tree_packed_dfs_amd.build`")
+    return C.CDLL(_LIB_PATH)
+
+
+lib = _load()
+
+_i32p = C.POINTER(C.c_int32)
+_i64p = C.POINTER(C.c_int64)
+_vp = C.c_void_p
+
+lib.tree_abi_version.restype = C.c_int
+lib.tree_status_string.restype = C.c_char_p
+lib.tree_status_string.argtypes = [C.c_int]
+lib.tree_last_error.restype = C.c_char_p
+lib.tree_build_trie.restype = C.c_int
+lib.tree_build_trie.argtypes = [C.c_int32, _i64p, _i32p, C.c_int32, _i32p, C.c_int64, _i64p, _i32p]
+lib.tree_pack_layout.restype = C.c_int
+lib.tree_pack_layout.argtypes = [C.c_int32, _i32p, C.c_int32, _i32p, C.c_int32, _i32p, _i32p, _i32p, _i64p,
+                                 _i32p, C.c_int64]
+lib.tree_validate_subtree_end.restype = C.c_int
+lib.tree_validate_subtree_end.argtypes = [_i32p, C.c_int64]
+lib.tree_rope.restype = C.c_int
+lib.tree_rope.argtypes = [C.c_int, _vp, C.c_int64, C.c_int64, C.c_int64, C.c_int64, _vp, C.c_float, _vp]
+lib.tree_attn_workspace_bytes.restype = C.c_size_t
+lib.tree_attn_workspace_bytes.argtypes = [C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
+                                          C.c_int]
+lib.tree_attn_fwd.restype = C.c_int
+lib.tree_attn_fwd.argtypes = [C.c_int, _vp, _vp, _vp, _vp, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
+                              C.c_int64, C.c_float, _vp, _vp, _vp, C.c_size_t, _vp]
+lib.tree_attn_bwd.restype = C.c_int
+lib.tree_attn_bwd.argtypes = [C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int64, C.c_int64, C.c_int64,
+                              C.c_int64, C.c_int64, C.c_float, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
+
+EXPORTED = ("tree_abi_version", "tree_status_string", "tree_last_error", "tree_build_trie",
+            "tree_pack_layout", "tree_validate_subtree_end", "tree_rope", "tree_attn_workspace_bytes",
+            "tree_attn_fwd", "tree_attn_bwd")
+
+
+def _check(status: int):
+    if status != 0:
+        name = lib.tree_status_string(status).decode()
+        msg = lib.tree_last_error().decode()
+        raise TreeAttnError(status, f"{name}: {msg}")
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(C.POINTER(ctype))
+
+
+# ---------------------------------------------------------------------------
+# host entry points
+# ---------------------------------------------------------------------------
+
+def tree_build_trie(sequences, min_shared: int = 64):
+    """Token sequences -> (parent int32 [n_nodes], seq_last int32 [n_seqs])."""
+    seqs = [np.ascontiguousarray(s, dtype=np.int32) for s in sequences]
+    lens = np.asarray([len(s) for s in seqs], dtype=np.int64)
+    offsets = np.zeros(len(seqs) + 1, dtype=np.int64)
+    np.cumsum(lens, out=offsets[1:])
+    tokens = np.concatenate(seqs) if seqs and offsets[-1] > 0 else np.zeros(1, dtype=np.int32)
+    total = int(offsets[-1])
+    parent = np.empty(max(total, 1), dtype=np.int32)
+    seq_last = np.empty(max(len(seqs), 1), dtype=np.int32)
+    n_nodes = C.c_int64(0)
+    _check(lib.tree_build_trie(len(seqs), _ptr(offsets, C.c_int64), _ptr(tokens, C.c_int32), int(min_shared),
+                               _ptr(parent, C.c_int32), total, C.byref(n_nodes), _ptr(seq_last, C.c_int32)))
+    return parent[:n_nodes.value].copy(), seq_last[:len(seqs)].copy()
+
+
+@dataclass
+class PackedLayout:
+    slot_node: np.ndarray      # [row_len] int32
+    pos_ids: np.ndarray        # [row_len] int32
+    subtree_end: np.ndarray    # [row_len] int32
+    seq_offsets: np.ndarray    # [n_seqs+1] int64
+    token_index: np.ndarray    # [seq_offsets[-1]] int32
+
+    def sequence_slots(self, s: int) -> np.ndarray:
+        return self.token_index[self.seq_offsets[s]:self.seq_offsets[s + 1]]
+
+
+def tree_pack_layout(parent, seq_last, row_len: int) -> PackedLayout:
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    seq_last = np.ascontiguousarray(seq_last, dtype=np.int32)
+    n, ns = len(parent), len(seq_last)
+    slot_node = np.empty(max(row_len, 1), dtype=np.int32)
+    pos_ids = np.empty(max(row_len, 1), dtype=np.int32)
+    se = np.empty(max(row_len, 1), dtype=np.int32)
+    offs = np.empty(ns + 1, dtype=np.int64)
+    pp = _ptr(parent if n else np.zeros(1, np.int32), C.c_int32)
+    sp = _ptr(seq_last if ns else np.zeros(1, np.int32), C.c_int32)
+    _check(lib.tree_pack_layout(n, pp, ns, sp, int(row_len), _ptr(slot_node, C.c_int32), _ptr(pos_ids, C.c_int32),
+                                _ptr(se, C.c_int32), _ptr(offs, C.c_int64), None, 0))
+    ti = np.empty(max(int(offs[-1]), 1), dtype=np.int32)
+    _check(lib.tree_pack_layout(n, pp, ns, sp, int(row_len), _ptr(slot_node, C.c_int32), _ptr(pos_ids, C.c_int32),
+                                _ptr(se, C.c_int32), _ptr(offs, C.c_int64), _ptr(ti, C.c_int32), len(ti)))
+    return PackedLayout(slot_node[:row_len], pos_ids[:row_len], se[:row_len], offs, ti[:int(offs[-1])])
+
+
+def tree_validate_subtree_end(subtree_end) -> None:
+    se = np.ascontiguousarray(subtree_end, dtype=np.int32)
+    _check(lib.tree_validate_subtree_end(_ptr(se if len(se) else np.zeros(1, np.int32), C.c_int32), len(se)))
+
+
+# ---------------------------------------------------------------------------
+# device entry points (torch tensors for memory and the current stream)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return TREE_F32
+    if t.dtype == torch.bfloat16:
+        return TREE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    torch = _torch()
+    return torch.cuda.current_stream().cuda_stream
+
+
+def tree_rope(x, pos_ids, theta: float = 10000.0):
+    """Rotate x [B, N, H, D] in place at depth pos_ids [B, N] (int32)."""
+    torch = _torch()
+    if x.dim() != 4:
+        raise ValueError("x must be [B, N, H, D]")
+    B, N, H, D = x.shape
+    if pos_ids.dtype != torch.int32 or tuple(pos_ids.shape) != (B, N):
+        raise ValueError("pos_ids must be int32 [B, N]")
+    _check(lib.tree_rope(_dtype_code(x), _dev(x, "x"), B, N, H, D, _dev(pos_ids, "pos_ids"), float(theta),
+                         _stream()))
+    return x
+
+
+def tree_attn_workspace_bytes(dtype_code: int, B, N, Hq, Hkv, D, bwd: bool) -> int:
+    return int(lib.tree_attn_workspace_bytes(int(dtype_code), B, N, Hq, Hkv, D, 1 if bwd else 0))
+
+
+def _shapes(q, k, v, subtree_end):
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, N, H, D]")
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, N, Hkv, D) or tuple(v.shape) != (B, N, Hkv, D):
+        raise ValueError("k, v must be [B, N, Hkv, D] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    if subtree_end.dtype != torch.int32 or tuple(subtree_end.shape) != (B, N):
+        raise ValueError("subtree_end must be int32 [B, N]")
+    return B, N, Hq, Hkv, D
+
+
+def _workspace(dt, B, N, Hq, Hkv, D, bwd, ws, device):
+    torch = _torch()
+    need = tree_attn_workspace_bytes(dt, B, N, Hq, Hkv, D, bwd)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    return ws
+
+
+def tree_attn_fwd(q, k, v, subtree_end, softmax_scale=None, out=None, lse=None, ws=None):
+    """Returns (out [B,N,Hq,D], lse [B,Hq,N] fp32)."""
+    torch = _torch()
+    B, N, Hq, Hkv, D = _shapes(q, k, v, subtree_end)
+    dt = _dtype_code(q)
+    scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    ws = _workspace(dt, B, N, Hq, Hkv, D, False, ws, q.device)
+    _check(lib.tree_attn_fwd(dt, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(subtree_end, "subtree_end"),
+                             B, N, Hq, Hkv, D, scale, _dev(out, "out"), _dev(lse, "lse"), ws.data_ptr(),
+                             ws.numel() * ws.element_size(), _stream()))
+    return out, lse
+
+
+def tree_attn_bwd(q, k, v, subtree_end, out, lse, dout, softmax_scale=None, dq=None, dk=None, dv=None, ws=None):
+    """Returns (dq, dk, dv)."""
+    torch = _torch()
+    B, N, Hq, Hkv, D = _shapes(q, k, v, subtree_end)
+    dt = _dtype_code(q)
+    scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
+    for t, nm in ((out, "out"), (dout, "dout")):
+        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype:
+            raise ValueError(f"{nm} must match q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("lse must be fp32 [B, Hq, N]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws = _workspace(dt, B, N, Hq, Hkv, D, True, ws, q.device)
+    _check(lib.tree_attn_bwd(dt, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(subtree_end, "subtree_end"),
+                             _dev(out, "out"), _dev(lse, "lse"), _dev(dout, "dout"), B, N, Hq, Hkv, D, scale,
+                             _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), ws.data_ptr(),
+                             ws.numel() * ws.element_size(), _stream()))
+    return dq, dk, dv

@@ -1,0 +1,301 @@
+// Vector-ALU attention kernels over a packed tree (the fp32 path).
+//
+// Mask: query i sees key j iff j <= i <= subtree_end[j] (the pre-order /
+// exit-order interval of [ART "Token-mixing layers"]; equivalently j is i or
+// one of its ancestors [DAG "The mask"]).  A 64-key tile whose largest
+// subtree_end is below the first query of the block has no visible pair and
+// is skipped whole.
+//
+// One thread owns one query row (forward, dq) or one key row (dk/dv); the
+// other side of the product is staged in LDS 64 rows at a time.  fp32
+// accumulation and softmax throughout.  These kernels serve the fp32 dtype,
+// whose tolerance (1e-5 relative) the bf16 matrix-core path cannot meet.
+#include "attn_vec.h"
+#include "device.h"
+
+#include <cmath>
+
+namespace treeattn {
+
+namespace {
+
+constexpr int TB = 64;  // rows per block = keys per tile
+
+template <typename T, int D>
+__global__ __launch_bounds__(TB) void vec_fwd(const T* __restrict__ q, const T* __restrict__ k,
+                                              const T* __restrict__ v, const int32_t* __restrict__ se,
+                                              int N, int Hq, int Hkv, float scale, T* __restrict__ out,
+                                              float* __restrict__ lse) {
+    __shared__ float ks[TB][D];
+    __shared__ float vs[TB][D];
+    __shared__ int ses[TB];
+    const int b = blockIdx.z, h = blockIdx.y, i0 = blockIdx.x * TB, t = threadIdx.x;
+    const int i = i0 + t;
+    const int g = h / (Hq / Hkv);
+    const int i_last = min(i0 + TB, N) - 1;
+    float qr[D], o[D];
+    const T* qp = q + (((int64_t)b * N + min(i, N - 1)) * Hq + h) * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        qr[d] = to_f32(qp[d]) * scale;
+        o[d] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+    const int32_t* ser = se + (int64_t)b * N;
+    for (int j0 = 0; j0 <= i_last; j0 += TB) {
+        const int j = j0 + t;
+        const int sej = j < N ? ser[j] : -1;
+        if (wave_max_i32(sej) < i0) continue;  // no key of this tile is visible to the block
+        ses[t] = sej;
+        for (int e = t; e < TB * D; e += TB) {
+            const int r = e / D, c = e % D, jj = j0 + r;
+            float kv = 0.f, vv = 0.f;
+            if (jj < N) {
+                const int64_t off = (((int64_t)b * N + jj) * Hkv + g) * D + c;
+                kv = to_f32(k[off]);
+                vv = to_f32(v[off]);
+            }
+            ks[r][c] = kv;
+            vs[r][c] = vv;
+        }
+        __syncthreads();
+        if (i < N) {
+            const int jn = min(TB, N - j0);
+            for (int r = 0; r < jn; ++r) {
+                const int jj = j0 + r;
+                if (jj > i || i > ses[r]) continue;
+                float s = 0.f;
+#pragma unroll
+                for (int d = 0; d < D; ++d) s = fmaf(qr[d], ks[r][d], s);
+                const float mn = fmaxf(m, s);
+                const float corr = expf(m - mn), p = expf(s - mn);
+                l = l * corr + p;
+#pragma unroll
+                for (int d = 0; d < D; ++d) o[d] = fmaf(p, vs[r][d], o[d] * corr);
+                m = mn;
+            }
+        }
+        __syncthreads();
+    }
+    if (i < N) {
+        const float inv = 1.f / l;
+        T* op = out + (((int64_t)b * N + i) * Hq + h) * D;
+#pragma unroll
+        for (int d = 0; d < D; ++d) op[d] = from_f32<T>(o[d] * inv);
+        lse[((int64_t)b * Hq + h) * N + i] = m + logf(l);
+    }
+}
+
+// delta[b,h,i] = sum_d dout * out (the row term of the softmax gradient)
+template <typename T, int D>
+__global__ __launch_bounds__(256) void vec_delta(const T* __restrict__ out, const T* __restrict__ dout,
+                                                 int64_t rows, int N, int Hq, float* __restrict__ delta) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // r = (b*N + i)*Hq + h
+    if (r >= rows) return;
+    const T* a = out + r * D;
+    const T* c = dout + r * D;
+    float s = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < D; ++d) s = fmaf(to_f32(a[d]), to_f32(c[d]), s);
+    const int h = (int)(r % Hq);
+    const int64_t bi = r / Hq;
+    const int64_t b = bi / N, i = bi % N;
+    delta[(b * Hq + h) * N + i] = s;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(TB) void vec_dq(const T* __restrict__ q, const T* __restrict__ k,
+                                             const T* __restrict__ v, const int32_t* __restrict__ se,
+                                             const float* __restrict__ lse, const float* __restrict__ delta,
+                                             const T* __restrict__ dout, int N, int Hq, int Hkv, float scale,
+                                             T* __restrict__ dq) {
+    __shared__ float ks[TB][D];
+    __shared__ float vs[TB][D];
+    __shared__ int ses[TB];
+    const int b = blockIdx.z, h = blockIdx.y, i0 = blockIdx.x * TB, t = threadIdx.x;
+    const int i = i0 + t;
+    const int g = h / (Hq / Hkv);
+    const int i_last = min(i0 + TB, N) - 1;
+    const int ic = min(i, N - 1);
+    float qr[D], dor[D], acc[D];
+    const T* qp = q + (((int64_t)b * N + ic) * Hq + h) * D;
+    const T* dp = dout + (((int64_t)b * N + ic) * Hq + h) * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        qr[d] = to_f32(qp[d]) * scale;
+        dor[d] = to_f32(dp[d]);
+        acc[d] = 0.f;
+    }
+    const float li = lse[((int64_t)b * Hq + h) * N + ic];
+    const float di = delta[((int64_t)b * Hq + h) * N + ic];
+    const int32_t* ser = se + (int64_t)b * N;
+    for (int j0 = 0; j0 <= i_last; j0 += TB) {
+        const int j = j0 + t;
+        const int sej = j < N ? ser[j] : -1;
+        if (wave_max_i32(sej) < i0) continue;
+        ses[t] = sej;
+        for (int e = t; e < TB * D; e += TB) {
+            const int r = e / D, c = e % D, jj = j0 + r;
+            float kv = 0.f, vv = 0.f;
+            if (jj < N) {
+                const int64_t off = (((int64_t)b * N + jj) * Hkv + g) * D + c;
+                kv = to_f32(k[off]);
+                vv = to_f32(v[off]);
+            }
+            ks[r][c] = kv;
+            vs[r][c] = vv;
+        }
+        __syncthreads();
+        if (i < N) {
+            const int jn = min(TB, N - j0);
+            for (int r = 0; r < jn; ++r) {
+                const int jj = j0 + r;
+                if (jj > i || i > ses[r]) continue;
+                float s = 0.f, dpv = 0.f;
+#pragma unroll
+                for (int d = 0; d < D; ++d) {
+                    s = fmaf(qr[d], ks[r][d], s);
+                    dpv = fmaf(dor[d], vs[r][d], dpv);
+                }
+                const float ds = expf(s - li) * (dpv - di);
+#pragma unroll
+                for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, ks[r][d], acc[d]);
+            }
+        }
+        __syncthreads();
+    }
+    if (i < N) {
+        T* o = dq + (((int64_t)b * N + i) * Hq + h) * D;
+#pragma unroll
+        for (int d = 0; d < D; ++d) o[d] = from_f32<T>(acc[d] * scale);
+    }
+}
+
+// One thread per key row of KV head g; loops over the query heads of the
+// group and over the queries i in [j, subtree_end[j]] (exactly the queries
+// that see key j), staged 64 at a time.
+template <typename T, int D>
+__global__ __launch_bounds__(TB) void vec_dkdv(const T* __restrict__ q, const T* __restrict__ k,
+                                               const T* __restrict__ v, const int32_t* __restrict__ se,
+                                               const float* __restrict__ lse, const float* __restrict__ delta,
+                                               const T* __restrict__ dout, int N, int Hq, int Hkv, float scale,
+                                               T* __restrict__ dk, T* __restrict__ dv) {
+    __shared__ float qs[TB][D];
+    __shared__ float dos[TB][D];
+    __shared__ float kr[TB][D + 1];  // own key and value rows, padded against bank conflicts
+    __shared__ float vr[TB][D + 1];
+    __shared__ float ls[TB], dls[TB];
+    const int b = blockIdx.z, g = blockIdx.y, j0 = blockIdx.x * TB, t = threadIdx.x;
+    const int j = j0 + t;
+    const int G = Hq / Hkv;
+    const int32_t* ser = se + (int64_t)b * N;
+    const int sej = j < N ? ser[j] : -1;
+    const int q_end = wave_max_i32(sej);  // last query any key of the block serves
+    for (int e = t; e < TB * D; e += TB) {
+        const int r = e / D, c = e % D, jj = j0 + r;
+        float kv = 0.f, vv = 0.f;
+        if (jj < N) {
+            const int64_t off = (((int64_t)b * N + jj) * Hkv + g) * D + c;
+            kv = to_f32(k[off]);
+            vv = to_f32(v[off]);
+        }
+        kr[r][c] = kv;
+        vr[r][c] = vv;
+    }
+    float adk[D], adv[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) adk[d] = adv[d] = 0.f;
+    __syncthreads();
+    for (int hh = 0; hh < G; ++hh) {
+        const int h = g * G + hh;
+        for (int i0 = j0; i0 <= q_end; i0 += TB) {
+            for (int e = t; e < TB * D; e += TB) {
+                const int r = e / D, c = e % D, ii = i0 + r;
+                float qv = 0.f, dv_ = 0.f;
+                if (ii < N) {
+                    const int64_t off = (((int64_t)b * N + ii) * Hq + h) * D + c;
+                    qv = to_f32(q[off]) * scale;
+                    dv_ = to_f32(dout[off]);
+                }
+                qs[r][c] = qv;
+                dos[r][c] = dv_;
+            }
+            {
+                const int ii = i0 + t;
+                ls[t] = ii < N ? lse[((int64_t)b * Hq + h) * N + ii] : 0.f;
+                dls[t] = ii < N ? delta[((int64_t)b * Hq + h) * N + ii] : 0.f;
+            }
+            __syncthreads();
+            if (j < N) {
+                const int rn = min(TB, N - i0);
+                for (int r = 0; r < rn; ++r) {
+                    const int ii = i0 + r;
+                    if (ii < j || ii > sej) continue;
+                    float s = 0.f, dpv = 0.f;
+#pragma unroll
+                    for (int d = 0; d < D; ++d) {
+                        s = fmaf(qs[r][d], kr[t][d], s);
+                        dpv = fmaf(dos[r][d], vr[t][d], dpv);
+                    }
+                    const float p = expf(s - ls[r]);
+                    const float ds = p * (dpv - dls[r]);
+#pragma unroll
+                    for (int d = 0; d < D; ++d) {
+                        adv[d] = fmaf(p, dos[r][d], adv[d]);
+                        adk[d] = fmaf(ds, qs[r][d], adk[d]);  // q already carries the scale
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (j < N) {
+        T* okp = dk + (((int64_t)b * N + j) * Hkv + g) * D;
+        T* ovp = dv + (((int64_t)b * N + j) * Hkv + g) * D;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            okp[d] = from_f32<T>(adk[d]);
+            ovp[d] = from_f32<T>(adv[d]);
+        }
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_fwd(const AttnArgs& a, hipStream_t st) {
+    dim3 grid((a.N + TB - 1) / TB, a.Hq, a.B), block(TB);
+    hipLaunchKernelGGL((vec_fwd<T, D>), grid, block, 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                       a.se, a.N, a.Hq, a.Hkv, a.scale, (T*)a.out, a.lse);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_bwd(const AttnArgs& a, float* delta, hipStream_t st) {
+    const int64_t rows = (int64_t)a.B * a.N * a.Hq;
+    hipLaunchKernelGGL((vec_delta<T, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
+                       (const T*)a.out, (const T*)a.dout, rows, a.N, a.Hq, delta);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 gq((a.N + TB - 1) / TB, a.Hq, a.B), gk((a.N + TB - 1) / TB, a.Hkv, a.B), block(TB);
+    hipLaunchKernelGGL((vec_dq<T, D>), gq, block, 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.se,
+                       a.lse, delta, (const T*)a.dout, a.N, a.Hq, a.Hkv, a.scale, (T*)a.dq);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((vec_dkdv<T, D>), gk, block, 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.se,
+                       a.lse, delta, (const T*)a.dout, a.N, a.Hq, a.Hkv, a.scale, (T*)a.dk, (T*)a.dv);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t vec_attn_fwd(const AttnArgs& a, hipStream_t st) {
+    if (a.dt == TREE_F32) return a.D == 64 ? launch_fwd<float, 64>(a, st) : launch_fwd<float, 128>(a, st);
+    return a.D == 64 ? launch_fwd<__bf16, 64>(a, st) : launch_fwd<__bf16, 128>(a, st);
+}
+
+hipError_t vec_attn_bwd(const AttnArgs& a, float* delta, hipStream_t st) {
+    if (a.dt == TREE_F32)
+        return a.D == 64 ? launch_bwd<float, 64>(a, delta, st) : launch_bwd<float, 128>(a, delta, st);
+    return a.D == 64 ? launch_bwd<__bf16, 64>(a, delta, st) : launch_bwd<__bf16, 128>(a, delta, st);
+}
+
+}  // namespace treeattn

@@ -10,4 +10,5 @@ from .workloads import (  # noqa: F401
     standard,
     round_bf16,
     feature_tables,
+    from_sequences,
 )

@@ -261,6 +261,33 @@ def long_history(seed_base: int = 5000, prefix: int = 20000, n: int = 8, unique:
     return _finish("long_history", tree, Hq, Hkv, D, dtype, row_len, seed_base)
 
 
+def from_sequences(sequences, *, Hq: int, Hkv: int, D: int, dtype: str, seed_base: int,
+                   row_len: Optional[int] = None, backward: bool = True, theta: float = 10000.0,
+                   name: str = "custom") -> Workload:
+    """A workload from explicit token sequences (any overlap pattern, e.g. a tiny vocabulary).
+
+    Feature rows are assigned per distinct prefix and gradient rows per
+    distinct (prefix, next token or end), with plain dictionaries.
+    """
+    seqs = [np.asarray(s, dtype=np.int32) for s in sequences]
+    pre: dict = {}
+    nxt: dict = {}
+    fids, dkeys = [], []
+    for s in seqs:
+        toks = s.tolist()
+        f = np.empty(len(toks), dtype=np.int64)
+        d = np.empty(len(toks), dtype=np.int64)
+        for t in range(len(toks)):
+            f[t] = pre.setdefault(tuple(toks[:t + 1]), len(pre))
+            key = tuple(toks[:t + 2]) if t + 1 < len(toks) else (tuple(toks), "end")
+            d[t] = nxt.setdefault(key, len(nxt))
+        fids.append(f)
+        dkeys.append(d)
+    return Workload(name=name, sequences=seqs, fid=fids, dkey=dkeys, n_feat=max(len(pre), 1),
+                    n_dkey=max(len(nxt), 1), Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, row_len=row_len,
+                    theta=theta, backward=backward, seed_base=seed_base)
+
+
 def standard(c: int) -> Workload:
     """The five workloads at their full sizes (c = 1..5)."""
     if c == 1:

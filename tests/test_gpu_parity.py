@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path through the C ABI against the oracle.
+
+Every case prints its name, seed and shape before touching the GPU.
+"""
+
+import numpy as np
+import pytest
+
+from synth import (agentic_trie, feature_tables, from_sequences, grpo_group, independent, long_history,
+                   standard, tiny_tree)
+
+from .pipeline import assert_within, compare, log, run_library, run_oracle, timed
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import prefix_tree_packed_dfs_amd  # noqa: F401  (fails loudly if the library is not built)
+    yield
+
+
+def _random_workload(seed, dtype, Hq, Hkv, D, n_seqs=6, max_len=300, vocab=2, fork_every=40):
+    """Sequences over a small alphabet of long runs: many forks, short and long shared runs."""
+    rng = np.random.default_rng(seed)
+    seqs = []
+    for _ in range(n_seqs):
+        L = int(rng.integers(1, max_len))
+        # runs of a repeated symbol: agreement over long stretches, then forks
+        s = np.repeat(rng.integers(0, vocab, size=L // fork_every + 1), fork_every)[:L]
+        seqs.append(s.astype(np.int32))
+    return from_sequences(seqs, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, seed_base=10_000 + seed)
+
+
+def _run_full(w, rope=True, label=""):
+    log(f"case {label or w.name}: dtype={w.dtype} Hq={w.Hq} Hkv={w.Hkv} D={w.D} seqs={len(w.sequences)} "
+        f"raw={w.raw_tokens} seed={w.seed_base}")
+    tables = feature_tables(w)
+    lres = timed("library", run_library, w, tables, rope=rope)
+    ores = timed("oracle", run_oracle, w, tables, rope=rope, R=lres.R)
+    rows = compare(w, lres, ores)
+    assert_within(w, rows)
+    return lres, ores
+
+
+# ---------------------------------------------------------------------------
+# rotary embedding alone
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
+def test_rope_matches_oracle(dtype, D):
+    import torch
+
+    import prefix_tree_packed_dfs_amd as lib
+    from oracle.precision import round_to
+    from oracle.rope import rope
+
+    log(f"case rope dtype={dtype} D={D}")
+    rng = np.random.default_rng(D)
+    N, H = 1000, 3
+    x = rng.standard_normal((N, H, D)).astype(np.float32)
+    pos = rng.integers(0, 40000, size=N).astype(np.int32)
+    pos[:5] = [0, 1, 2, 36863, 32767]
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    xt = torch.from_numpy(x).to(tdt)
+    x_in = xt.to(torch.float64).numpy()
+    dev = xt.view(1, N, H, D).cuda()
+    lib.tree_rope(dev, torch.from_numpy(pos).view(1, N).cuda(), 10000.0)
+    got = dev[0].to(torch.float64).cpu().numpy()
+    want = round_to(rope(x_in, pos, 10000.0), dtype)
+    ulp = np.abs(want) * (2.0**-23 if dtype == "f32" else 2.0**-7) + 1e-30
+    diff = np.abs(got - want)
+    log(f"    exact {np.mean(diff == 0):.6f}, max diff/ulp {np.max(diff / ulp):.3f}")
+    assert np.all(diff <= ulp * 1.0001)
+    assert np.mean(diff == 0) > 0.999
+    assert np.array_equal(got[pos == 0], x_in[pos == 0])
+
+
+# ---------------------------------------------------------------------------
+# small trees, every element compared
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_trees_f32(seed):
+    w = _random_workload(seed, "f32", Hq=2, Hkv=2, D=64)
+    _run_full(w, label=f"random_tree_f32[{seed}]")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_trees_bf16_gqa(seed):
+    w = _random_workload(100 + seed, "bf16", Hq=4, Hkv=2, D=128)
+    _run_full(w, label=f"random_tree_bf16[{seed}]")
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_random_tree_bf16_no_rope_and_rope(rope):
+    w = _random_workload(500, "bf16", Hq=8, Hkv=2, D=128, n_seqs=9, max_len=700)
+    _run_full(w, rope=rope, label=f"random_tree_bf16_rope={rope}")
+
+
+def test_degenerate_rows():
+    # a single token; a single chain shorter than a tile; a row that is all padding but one slot
+    for seqs in ([[5]], [list(range(37))], [[1, 2], [1, 3]]):
+        w = from_sequences(seqs, Hq=2, Hkv=1, D=128, dtype="bf16", seed_base=77, row_len=130)
+        _run_full(w, label=f"degenerate{[len(s) for s in seqs]}")
+
+
+# ---------------------------------------------------------------------------
+# the five workloads, shrunk: same structure and head shapes, several tiles and ragged tails
+# ---------------------------------------------------------------------------
+
+SHRUNK = {
+    "tiny_tree": lambda: tiny_tree(),
+    "grpo_group": lambda: grpo_group(prompt=300, n=5, completion=150, row_len=None),
+    "agentic_trie": lambda: agentic_trie(budget=3000, seg_lo=64, seg_hi=400, ratio_lo=1.5, ratio_hi=9.0,
+                                         row_len=3072),
+    "independent": lambda: independent(n=7, length=200, row_len=1408),
+    "long_history": lambda: long_history(prefix=1000, n=4, unique=300, row_len=None),
+}
+
+
+@pytest.mark.parametrize("name", list(SHRUNK))
+def test_shrunk_workloads(name):
+    _run_full(SHRUNK[name](), label=f"shrunk_{name}")
+
+
+# ---------------------------------------------------------------------------
+# full sizes
+# ---------------------------------------------------------------------------
+
+def test_full_c1_tiny_fp32():
+    _run_full(standard(1), label="full_tiny_tree")
+
+
+def test_full_c2_grpo():
+    _run_full(standard(2), label="full_grpo_group")
+
+
+def test_full_c4_independent():
+    _run_full(standard(4), label="full_independent")
+
+
+def _run_sampled(w, label, n_q=256, tail=256):
+    from oracle.layout import dfs_layout
+    from oracle.trie import build_trie
+
+    log(f"case {label}: dtype={w.dtype} Hq={w.Hq} Hkv={w.Hkv} D={w.D} seqs={len(w.sequences)} "
+        f"raw={w.raw_tokens} (sampled)")
+    tables = feature_tables(w)
+    lres = timed("library", run_library, w, tables)
+    trie = build_trie(w.sequences)
+    olay = dfs_layout(trie.parent, trie.seq_last, lres.R)
+    rng = np.random.default_rng(w.seed_base)
+    qs_lib, qs_ora, ks_lib, ks_ora = [], [], [], []
+    for _ in range(n_q):                     # uniformly random tokens: out, lse, dq
+        s = int(rng.integers(len(w.sequences)))
+        t = int(rng.integers(len(w.sequences[s])))
+        qs_lib.append(lres.layout.sequence_slots(s)[t])
+        qs_ora.append(olay.token_index[s][t])
+    for s in range(len(w.sequences)):        # keys near the end of every sequence: dk, dv
+        L = len(w.sequences[s])
+        for t in rng.choice(np.arange(max(0, L - tail), L), size=min(16, L), replace=False):
+            ks_lib.append(lres.layout.sequence_slots(s)[t])
+            ks_ora.append(olay.token_index[s][t])
+    ores = timed("oracle", run_oracle, w, tables, R=lres.R, q_slots=np.unique(qs_ora), k_slots=np.unique(ks_ora))
+    rows = compare(w, lres, ores, lib_slots=np.unique(qs_lib), key_slots=np.unique(ks_lib))
+    assert_within(w, rows)
+    # properties that hold at any size, over every slot
+    n = lres.n
+    G = w.Hq // w.Hkv
+    do_sum = _dout_sum(w, tables, lres)
+    assert np.allclose(lres.dv[:n].sum(axis=0), do_sum, atol=0.05 * np.abs(do_sum).max() + 0.5)
+    assert np.abs(lres.dk[:n].sum(axis=0)).max() < 0.05 * np.sqrt(n * G)
+    assert np.all(np.isfinite(lres.out[:n])) and np.all(np.isfinite(lres.dq[:n]))
+
+
+def _dout_sum(w, tables, lres):
+    """Sum over packed slots of dout, per KV head group: equals sum_j dV[j] (softmax rows sum to one)."""
+    from .pipeline import slot_rows
+    _, dkey_slot = slot_rows(w, lres.layout, lres.n)
+    do = tables["do"][dkey_slot[:lres.n]].astype(np.float64)
+    return do.reshape(lres.n, w.Hkv, w.Hq // w.Hkv, w.D).sum(axis=(0, 2))
+
+
+def test_full_c3_agentic_sampled():
+    _run_sampled(standard(3), "full_agentic_trie")
+
+
+def test_full_c5_long_history_sampled():
+    _run_sampled(standard(5), "full_long_history")
+
+
+# ---------------------------------------------------------------------------
+# batch of rows, determinism
+# ---------------------------------------------------------------------------
+
+def test_batch_rows_are_independent_and_deterministic():
+    import torch
+
+    import prefix_tree_packed_dfs_amd as lib
+    log("case batch_of_two_rows")
+    R = 1024
+    rows = []
+    for seed in (1, 2):
+        w = _random_workload(900 + seed, "bf16", Hq=4, Hkv=2, D=128, n_seqs=5, max_len=500)
+        parent, seq_last = lib.tree_build_trie(w.sequences)
+        lay = lib.tree_pack_layout(parent, seq_last, R)
+        rows.append(lay.subtree_end)
+    g = torch.Generator().manual_seed(3)
+    q = torch.randn(2, R, 4, 128, generator=g).to(torch.bfloat16).cuda()
+    k = torch.randn(2, R, 2, 128, generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn(2, R, 2, 128, generator=g).to(torch.bfloat16).cuda()
+    do = torch.randn(2, R, 4, 128, generator=g).to(torch.bfloat16).cuda()
+    se = torch.from_numpy(np.stack(rows).astype(np.int32)).cuda()
+    out, lse = lib.tree_attn_fwd(q, k, v, se)
+    grads = lib.tree_attn_bwd(q, k, v, se, out, lse, do)
+    out2, lse2 = lib.tree_attn_fwd(q, k, v, se)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    for b in range(2):
+        o1, l1 = lib.tree_attn_fwd(q[b:b + 1].contiguous(), k[b:b + 1].contiguous(), v[b:b + 1].contiguous(),
+                                   se[b:b + 1].contiguous())
+        assert torch.equal(o1[0], out[b]) and torch.equal(l1[0], lse[b])
+        g1 = lib.tree_attn_bwd(q[b:b + 1].contiguous(), k[b:b + 1].contiguous(), v[b:b + 1].contiguous(),
+                               se[b:b + 1].contiguous(), o1, l1, do[b:b + 1].contiguous())
+        for x, y in zip(g1, grads):
+            assert torch.allclose(x[0].float(), y[b].float(), atol=1e-2, rtol=0)

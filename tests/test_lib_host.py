@@ -1,0 +1,164 @@
+"""The C-ABI library on the CPU: symbols, host integer path vs the oracle (bit-exact), error codes."""
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import prefix_tree_packed_dfs_amd as lib
+from oracle.layout import dfs_layout
+from oracle.trie import build_trie
+from synth import standard
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "tree_attn.h")).read()
+    declared = set(re.findall(r"\b(tree_[a-z_]+)\s*\(", header))
+    assert declared, "no declarations found"
+    assert declared == set(lib.EXPORTED)
+    for name in declared:
+        assert hasattr(lib.lib, name), name
+    assert lib.lib.tree_abi_version() == 1
+
+
+def _random_sequences(rng, n, max_len, vocab):
+    return [rng.integers(0, vocab, size=int(rng.integers(0, max_len))).astype(np.int32) for _ in range(n)]
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_build_trie_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    seqs = _random_sequences(rng, int(rng.integers(1, 12)), 30, int(rng.integers(2, 5)))
+    seqs = [s for s in seqs if len(s)] or [np.array([1], np.int32)]
+    for ms in (1, 2, 3, 64):
+        ref = build_trie(seqs, min_shared=ms)
+        parent, seq_last = lib.tree_build_trie(seqs, min_shared=ms)
+        assert np.array_equal(parent, ref.parent)
+        assert np.array_equal(seq_last, ref.seq_last)
+
+
+def test_build_trie_empty_sequences():
+    parent, seq_last = lib.tree_build_trie([[], [5, 6], []], min_shared=1)
+    assert parent.tolist() == [-1, 0] and seq_last.tolist() == [-1, 1, -1]
+    parent, seq_last = lib.tree_build_trie([], min_shared=1)
+    assert len(parent) == 0 and len(seq_last) == 0
+
+
+@pytest.mark.parametrize("c", [1, 2, 3, 4, 5])
+def test_workload_tries_and_layouts_match_oracle(c):
+    w = standard(c)
+    ref = build_trie(w.sequences)
+    parent, seq_last = lib.tree_build_trie(w.sequences, min_shared=64)
+    assert np.array_equal(parent, ref.parent) and np.array_equal(seq_last, ref.seq_last)
+    R = w.row_length(len(parent))
+    lay = lib.tree_pack_layout(parent, seq_last, R)
+    rl = dfs_layout(ref.parent, ref.seq_last, R)
+    assert np.array_equal(lay.slot_node, rl.slot_node)
+    assert np.array_equal(lay.pos_ids, rl.pos_ids)
+    assert np.array_equal(lay.subtree_end, rl.subtree_end)
+    for s in range(len(w.sequences)):
+        assert np.array_equal(lay.sequence_slots(s), rl.token_index[s])
+    lib.tree_validate_subtree_end(lay.subtree_end)
+
+
+def _random_forest(rng, n):
+    parent = np.full(n, -1, dtype=np.int64)
+    for v in range(1, n):
+        parent[v] = -1 if rng.random() < 0.15 else int(rng.integers(0, v))
+    perm = rng.permutation(n)
+    inv = np.empty(n, dtype=np.int64)
+    inv[perm] = np.arange(n)
+    out = np.full(n, -1, dtype=np.int32)
+    for v in range(n):
+        if parent[v] >= 0:
+            out[inv[v]] = inv[parent[v]]
+    return out
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_pack_layout_matches_oracle_on_any_numbering(seed):
+    rng = np.random.default_rng(1000 + seed)
+    n = int(rng.integers(0, 200))
+    parent = _random_forest(rng, n)
+    seq_last = rng.integers(-1, max(n, 1), size=int(rng.integers(0, 10))).astype(np.int32) if n else \
+        np.zeros(0, np.int32)
+    R = n + int(rng.integers(0, 7))
+    lay = lib.tree_pack_layout(parent, seq_last, R)
+    rl = dfs_layout(parent, seq_last, R)
+    assert np.array_equal(lay.slot_node, rl.slot_node)
+    assert np.array_equal(lay.pos_ids, rl.pos_ids)
+    assert np.array_equal(lay.subtree_end, rl.subtree_end)
+    for s in range(len(seq_last)):
+        assert np.array_equal(lay.sequence_slots(s), rl.token_index[s])
+
+
+def test_pack_layout_deep_chain():
+    n = 40000
+    parent = np.arange(-1, n - 1, dtype=np.int32)
+    lay = lib.tree_pack_layout(parent, np.array([n - 1], np.int32), n)
+    assert lay.pos_ids[-1] == n - 1 and lay.subtree_end[0] == n - 1
+    assert np.array_equal(lay.token_index, np.arange(n))
+
+
+def _status(fn):
+    with pytest.raises(lib.TreeAttnError) as e:
+        fn()
+    return e.value.status
+
+
+def test_error_codes():
+    assert _status(lambda: lib.tree_pack_layout([1, 0], [0], 2)) == 2           # cycle
+    assert _status(lambda: lib.tree_pack_layout([-1, 7], [1], 2)) == 2          # parent out of range
+    assert _status(lambda: lib.tree_pack_layout([-1, 1], [1], 2)) == 2          # self parent
+    assert _status(lambda: lib.tree_pack_layout([-1, 0, 1], [2], 2)) == 3       # row too short
+    assert _status(lambda: lib.tree_pack_layout([-1, 0], [5], 2)) == 2          # seq_last out of range
+    assert _status(lambda: lib.tree_build_trie([[1, 2]], min_shared=0)) == 1
+    assert _status(lambda: lib.tree_validate_subtree_end([0, 5])) == 2          # beyond the row
+    assert _status(lambda: lib.tree_validate_subtree_end([2, 3, 2, 3])) == 2    # crossing intervals
+    assert _status(lambda: lib.tree_validate_subtree_end([1, 0])) == 2          # before its own slot
+    lib.tree_validate_subtree_end([3, 1, 3, 3])
+    lib.tree_validate_subtree_end([])
+
+
+def test_capacity_and_size_query():
+    L = lib.lib
+    offs = np.array([0, 3, 6], dtype=np.int64)
+    toks = np.array([1, 2, 3, 1, 2, 4], dtype=np.int32)
+    n = C.c_int64(0)
+    i32 = C.POINTER(C.c_int32)
+    st = L.tree_build_trie(2, offs.ctypes.data_as(C.POINTER(C.c_int64)), toks.ctypes.data_as(i32), 1, None, 0,
+                           C.byref(n), None)
+    assert st == 0 and n.value == 1 + 2 * 2
+    small = np.zeros(2, np.int32)
+    st = L.tree_build_trie(2, offs.ctypes.data_as(C.POINTER(C.c_int64)), toks.ctypes.data_as(i32), 1,
+                           small.ctypes.data_as(i32), 2, C.byref(n), None)
+    assert st == 3 and n.value == 5
+    parent = np.array([-1, 0, 0], np.int32)
+    seq_last = np.array([1, 2], np.int32)
+    R = 3
+    a = [np.zeros(R, np.int32) for _ in range(3)]
+    offsets = np.zeros(3, np.int64)
+    ti = np.zeros(3, np.int32)
+    st = L.tree_pack_layout(3, parent.ctypes.data_as(i32), 2, seq_last.ctypes.data_as(i32), R,
+                            *(x.ctypes.data_as(i32) for x in a), offsets.ctypes.data_as(C.POINTER(C.c_int64)),
+                            ti.ctypes.data_as(i32), 3)
+    assert st == 3 and offsets.tolist() == [0, 2, 4]
+
+
+def test_device_entry_points_reject_bad_arguments_before_any_launch():
+    L = lib.lib
+    # unsupported head dim / dtype / head ratio: refused by the host checks, nothing enqueued
+    assert L.tree_attn_fwd(1, None, None, None, None, 1, 8, 4, 2, 96, 1.0, None, None, None, 0, None) == 4
+    assert L.tree_attn_fwd(7, None, None, None, None, 1, 8, 4, 2, 64, 1.0, None, None, None, 0, None) == 1
+    assert L.tree_attn_fwd(1, None, None, None, None, 1, 8, 6, 4, 64, 1.0, None, None, None, 0, None) == 1
+    assert L.tree_attn_fwd(1, None, None, None, None, 1, 8, 4, 2, 64, 1.0, None, None, None, 0, None) == 1
+    assert L.tree_attn_bwd(1, *([None] * 7), 1, 8, 4, 2, 64, 1.0, None, None, None, None, 0, None) == 1
+    assert L.tree_rope(1, None, 1, 8, 4, 80, None, 1e4, None) == 4
+    assert L.tree_rope(1, None, 1, 8, 4, 64, None, -1.0, None) == 1
+    assert L.tree_attn_workspace_bytes(1, 1, 8, 4, 2, 96, 1) == 0
+    # empty batches are a no-op
+    assert L.tree_attn_fwd(1, None, None, None, None, 0, 8, 4, 2, 64, 1.0, None, None, None, 0, None) == 0
