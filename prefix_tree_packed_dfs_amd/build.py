@@ -23,6 +23,7 @@ SOURCES = [
     "attn_api.cpp",
     "rope.hip",
     "attn_vec.hip",
+    "attn_mfma_fwd.hip",
 ]
 
 # Packed-fp32 VALU ops are turned off for device code (the compiler would

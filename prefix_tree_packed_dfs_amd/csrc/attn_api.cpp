@@ -3,6 +3,7 @@
 
 #include <cmath>
 
+#include "attn_mfma.h"
 #include "attn_vec.h"
 #include "common.h"
 
@@ -27,7 +28,13 @@ tree_status check_shapes(tree_dtype dt, int64_t B, int64_t N, int64_t Hq, int64_
     return TREE_OK;
 }
 
-size_t fwd_ws(tree_dtype, int64_t, int64_t, int64_t, int64_t, int64_t) { return 0; }
+bool use_mfma(tree_dtype dt, int64_t Hq, int64_t Hkv, int64_t D) {
+    return dt == TREE_BF16 && mfma_supported((int)D, (int)(Hq / Hkv));
+}
+
+size_t fwd_ws(tree_dtype dt, int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t D) {
+    return use_mfma(dt, Hq, Hkv, D) ? mfma_fwd_ws_bytes((int)B, (int)N, (int)Hkv, (int)D) : 0;
+}
 
 size_t bwd_ws(tree_dtype, int64_t B, int64_t N, int64_t Hq, int64_t, int64_t) {
     return align_up((size_t)B * Hq * N * sizeof(float));  // delta
@@ -61,6 +68,9 @@ extern "C" tree_status tree_attn_fwd(tree_dtype dt, const void* q, const void* k
         return fail(TREE_ERR_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
     AttnArgs a{dt, q, k, v, subtree_end, (int)B, (int)N, (int)Hq, (int)Hkv, (int)D, softmax_scale,
                out, lse, nullptr, nullptr, nullptr, nullptr};
+    if (use_mfma(dt, Hq, Hkv, D))
+        return device_status(mfma_attn_fwd(a, carve_fwd_ws(ws, (int)B, (int)N, (int)Hkv, (int)D), (hipStream_t)stream),
+                             "tree_attn_fwd launch");
     return device_status(vec_attn_fwd(a, (hipStream_t)stream), "tree_attn_fwd launch");
 }
 

@@ -1,0 +1,31 @@
+// Matrix-core (MFMA) attention path for bf16: shared constants and launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "attn_vec.h"
+
+namespace treeattn {
+
+// Keys per KV tile and rows per MFMA block.
+constexpr int KT = 64;
+
+// Query heads one workgroup serves (all heads sharing a KV head, up to 8).
+inline int heads_per_wg(int G) { return G >= 8 ? 8 : G; }
+// Whether the MFMA path covers this shape (else the vector path runs).
+inline bool mfma_supported(int D, int G) {
+    return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G % 8 == 0);
+}
+
+// Workspace carved by the forward: per-tile subtree_end range and V transposed.
+struct FwdWorkspace {
+    int32_t* tile_min;   // [B, T]
+    int32_t* tile_max;   // [B, T]
+    __bf16* vt;          // [B, Hkv, D, T*KT], keys permuted inside each 16-key group
+};
+
+size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D);
+FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D);
+hipError_t mfma_attn_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st);
+
+}  // namespace treeattn

@@ -128,10 +128,11 @@ class Cmp:
     rel: float
     cos: float
     count: int
+    beyond_half_ulp: float   # max over elements of |a-b| - 2^-8 |b| (bf16 storage rounding taken out)
 
     def __str__(self):
-        return (f"{self.name:4s} max|d|={self.max_abs:.3e} max|ref|={self.max_ref:.3e} rel={self.rel:.3e} "
-                f"cos={self.cos:.8f} n={self.count}")
+        return (f"{self.name:8s} max|d|={self.max_abs:.3e} max|ref|={self.max_ref:.3e} rel={self.rel:.3e} "
+                f"cos={self.cos:.8f} beyond-half-ulp={self.beyond_half_ulp:.3e} n={self.count}")
 
 
 def cmp(name, a, b) -> Cmp:
@@ -143,13 +144,16 @@ def cmp(name, a, b) -> Cmp:
     ref = float(np.max(np.abs(b))) if b.size else 0.0
     den = float(np.linalg.norm(a) * np.linalg.norm(b))
     cos = float(a @ b / den) if den > 0 else 1.0
-    return Cmp(name, d, ref, d / ref if ref > 0 else d, cos, a.size)
+    beyond = float(np.max(np.abs(a - b) - 2.0**-8 * np.abs(b))) if a.size else 0.0
+    return Cmp(name, d, ref, d / ref if ref > 0 else d, cos, a.size, beyond)
 
 
 TOL = {
     # fp32: max|a-b| <= 1e-5 * max|b| per tensor
     "f32": {"rel": 1e-5},
-    # bf16: absolute bars on out/dq/dk/dv and lse, plus a relative max-norm bar
+    # bf16: 2e-2 absolute on out/dq/dk/dv on top of the half-ulp rounding of the bf16 output
+    # (|a-b| <= 2e-2 + 2^-8 |b| per element), 1e-3 absolute on the fp32 lse, and a relative
+    # max-norm bar of 2e-2 on every tensor
     "bf16": {"abs": 2e-2, "abs_lse": 1e-3, "rel": 2e-2},
 }
 
@@ -183,8 +187,10 @@ def assert_within(w, rows):
         if w.dtype == "f32":
             assert r.max_abs <= tol["rel"] * r.max_ref, f"{r.name}: {r}"
         else:
-            bar = tol["abs_lse"] if r.name == "lse" else tol["abs"]
-            assert r.max_abs <= bar, f"{r.name}: {r}"
+            if r.name == "lse":
+                assert r.max_abs <= tol["abs_lse"], f"{r.name}: {r}"
+            else:
+                assert r.beyond_half_ulp <= tol["abs"], f"{r.name}: {r}"
             assert r.rel <= tol["rel"], f"{r.name}: {r}"
 
 
