@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark one step of the prefix-tree-packed attention hot path on one MI355X.
+
+A step is one pass of the whole path over one packed row:
+  tree_pack_layout (host, into pinned buffers) -> async copy of pos_ids and
+  subtree_end -> tree_rope(q), tree_rope(k) -> tree_attn_fwd -> tree_attn_bwd.
+Inputs (q, k, v, dout) are resident in HBM before timing starts.
+
+Throughput is algorithmic: ancestor pairs per head = sum over real slots of
+(depth + 1); forward FLOPs = 4 * D * Hq * pairs, backward = 2.5 x forward.
+Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload grpo_group]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+WORKLOADS = {
+    "tiny_tree": 1,
+    "grpo_group": 2,
+    "agentic_trie": 3,
+    "independent": 4,
+    "long_history": 5,
+}
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def describe(w, n, R, pairs):
+    return {
+        "workload": w.name,
+        "sequences": len(w.sequences),
+        "row_len": R,
+        "forwarded_tokens": n,
+        "raw_tokens": w.raw_tokens,
+        "packing_ratio": round(w.raw_tokens / n, 4),
+        "ancestor_pairs_per_head": int(pairs),
+        "Hq": w.Hq,
+        "Hkv": w.Hkv,
+        "head_dim": w.D,
+        "batch_rows": 1,
+    }
+
+
+def cpu_baseline(w, total_flops, target_s):
+    """Time the oracle (fwd + bwd, fp64, CPU) on the first sequences of the workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.attention import tree_attention
+    from synth import feature_tables
+
+    tables = feature_tables(w)
+    # grow the sample until one run takes about target_s / 4, then time it
+    k = 1
+    raw_all = w.raw_tokens
+    while True:
+        seqs = w.sequences[:k]
+        t0 = time.perf_counter()
+        tree_attention(seqs, w.fid[:k], w.dkey[:k], tables, theta=w.theta, backward=True, storage=w.dtype)
+        dt = time.perf_counter() - t0
+        if dt > target_s / 4 or k == len(w.sequences):
+            break
+        k = min(len(w.sequences), max(k + 1, int(k * (target_s / 4) / max(dt, 1e-3))))
+    raw_k = sum(len(s) for s in seqs)
+    # the oracle's cost is per unpacked sequence: extrapolate by raw-token work share
+    work = lambda ss: sum(len(s) * (len(s) + 1) / 2 for s in ss)  # noqa: E731
+    frac = work(seqs) / work(w.sequences)
+    full_s = dt / frac
+    threads = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas") or 1
+    _ = np
+    return {
+        "value": round(total_flops / full_s / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"oracle fwd+bwd on the first {k} of {len(w.sequences)} sequences ({raw_k} of {raw_all} raw "
+                  f"tokens, {frac:.3f} of the oracle's per-sequence work) took {dt:.2f} s; whole-row time "
+                  f"extrapolated to {full_s:.1f} s",
+        "seconds_sample": round(dt, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="grpo_group", choices=list(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import ctypes as C
+
+    import numpy as np
+    import torch
+
+    import prefix_tree_packed_dfs_amd as lib
+    from synth import standard
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    w = standard(WORKLOADS[args.workload])
+    if not w.backward:
+        w.backward = True  # time the full path on every workload
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dt_code = lib.TREE_BF16 if w.dtype == "bf16" else lib.TREE_F32
+
+    # planner output (the trie) is the input of the path
+    parent, seq_last = lib.tree_build_trie(w.sequences, min_shared=64)
+    n = len(parent)
+    R = w.row_length(n)
+    lay = lib.tree_pack_layout(parent, seq_last, R)
+    pairs = int((lay.pos_ids[:n].astype(np.int64) + 1).sum())
+    fwd_flops = 4.0 * w.D * w.Hq * pairs
+    bwd_flops = 2.5 * fwd_flops
+    total_flops = fwd_flops + bwd_flops
+
+    g = torch.Generator(device=dev).manual_seed(2024)
+    q = torch.randn((1, R, w.Hq, w.D), generator=g, device=dev).to(tdt)
+    k = torch.randn((1, R, w.Hkv, w.D), generator=g, device=dev).to(tdt)
+    v = torch.randn((1, R, w.Hkv, w.D), generator=g, device=dev).to(tdt)
+    do = torch.randn((1, R, w.Hq, w.D), generator=g, device=dev).to(tdt)
+    out = torch.empty_like(q)
+    lse = torch.empty((1, w.Hq, R), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    pos_d = torch.empty((1, R), device=dev, dtype=torch.int32)
+    se_d = torch.empty((1, R), device=dev, dtype=torch.int32)
+    wsf = torch.empty(max(lib.tree_attn_workspace_bytes(dt_code, 1, R, w.Hq, w.Hkv, w.D, False), 1),
+                      device=dev, dtype=torch.uint8)
+    wsb = torch.empty(max(lib.tree_attn_workspace_bytes(dt_code, 1, R, w.Hq, w.Hkv, w.D, True), 1),
+                      device=dev, dtype=torch.uint8)
+
+    # pinned, double-buffered host layout buffers
+    parent_h = np.ascontiguousarray(parent, dtype=np.int32)
+    seq_last_h = np.ascontiguousarray(seq_last, dtype=np.int32)
+    ti_cap = int(lay.seq_offsets[-1])
+    bufs = []
+    for _ in range(2):
+        pos_p = torch.empty(R, dtype=torch.int32, pin_memory=True)
+        se_p = torch.empty(R, dtype=torch.int32, pin_memory=True)
+        bufs.append({"pos": pos_p, "se": se_p, "slot": np.empty(R, np.int32),
+                     "off": np.empty(len(seq_last_h) + 1, np.int64), "ti": np.empty(max(ti_cap, 1), np.int32),
+                     "ev": torch.cuda.Event()})
+    i32 = C.POINTER(C.c_int32)
+    i64 = C.POINTER(C.c_int64)
+    stream = torch.cuda.current_stream()
+    scale = w.D ** -0.5
+    host_ms = []
+
+    def ptr(a, t):
+        return a.ctypes.data_as(t)
+
+    def step(i, timing=None):
+        bf = bufs[i % 2]
+        bf["ev"].synchronize()  # the copy that last read these pinned buffers is done
+        t0 = time.perf_counter()
+        st = lib.lib.tree_pack_layout(n, ptr(parent_h, i32), len(seq_last_h), ptr(seq_last_h, i32), R,
+                                      ptr(bf["slot"], i32), C.cast(bf["pos"].data_ptr(), i32),
+                                      C.cast(bf["se"].data_ptr(), i32), ptr(bf["off"], i64), ptr(bf["ti"], i32),
+                                      ti_cap)
+        host_ms.append(1e3 * (time.perf_counter() - t0))
+        assert st == 0
+        pos_d.view(-1).copy_(bf["pos"], non_blocking=True)
+        se_d.view(-1).copy_(bf["se"], non_blocking=True)
+        bf["ev"].record(stream)
+        if timing:
+            timing[0].record(stream)
+        lib.tree_rope(q, pos_d, w.theta)
+        lib.tree_rope(k, pos_d, w.theta)
+        if timing:
+            timing[1].record(stream)
+        lib.tree_attn_fwd(q, k, v, se_d, scale, out=out, lse=lse, ws=wsf)
+        if timing:
+            timing[2].record(stream)
+        lib.tree_attn_bwd(q, k, v, se_d, out, lse, do, scale, dq=dq, dk=dk, dv=dv, ws=wsb)
+        if timing:
+            timing[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    host_ms.clear()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / args.steps
+    rope_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    bwd_tf = bwd_flops / (bwd_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "tree-attn fwd+bwd ancestor-pair TFLOP/s & forwarded tok/s, 32K row, 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": describe(w, n, R, pairs),
+        "forwarded_tok_s": round(n / (ms_step * 1e-3), 1),
+        "raw_tok_s": round(w.raw_tokens / (ms_step * 1e-3), 1),
+        "breakdown_ms": {"rope_q_k": round(rope_ms, 4), "fwd": round(fwd_ms, 4), "bwd": round(bwd_ms, 4),
+                         "host_layout": round(float(np.mean(host_ms)), 4)},
+        "tflops_fwd": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 3),
+        "tflops_bwd": round(bwd_tf, 3),
+        "frac_of_bf16_peak_step": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": {
+            "kernel": "tree_attn_bwd (every kernel of the call)",
+            "bound": "mfma",
+            "achieved": round(bwd_tf, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, total_flops, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,7 @@ inline bool mfma_supported(int D, int G) {
 struct FwdWorkspace {
     int32_t* tile_min;   // [B, T]
     int32_t* tile_max;   // [B, T]
-    __bf16* vt;          // [B, Hkv, D, T*KT], keys permuted inside each 16-key group
+    uint16_t* vt;        // bf16 bits [B, Hkv, D, T*KT], keys permuted inside each 16-key group
 };
 
 size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D);

@@ -336,7 +336,7 @@ template <int D>
 hipError_t launch_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
     hipLaunchKernelGGL((fwd_prep<D>), dim3(T, a.Hkv, a.B), dim3(256), 0, st, (const __bf16*)a.v, a.se, a.N, a.Hkv,
-                       T, w.tile_min, w.tile_max, w.vt);
+                       T, w.tile_min, w.tile_max, (__bf16*)w.vt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     switch (heads_per_wg(a.Hq / a.Hkv)) {
@@ -364,7 +364,7 @@ FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D) {
     p += align256((size_t)B * T * sizeof(int32_t));
     w.tile_max = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)B * T * sizeof(int32_t));
-    w.vt = reinterpret_cast<__bf16*>(p);
+    w.vt = reinterpret_cast<uint16_t*>(p);
     (void)Hkv;
     (void)D;
     return w;
