@@ -24,6 +24,7 @@ SOURCES = [
     "rope.hip",
     "attn_vec.hip",
     "attn_mfma_fwd.hip",
+    "attn_mfma_bwd.hip",
 ]
 
 # Packed-fp32 VALU ops are turned off for device code (the compiler would

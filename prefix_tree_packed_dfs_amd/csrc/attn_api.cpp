@@ -36,7 +36,8 @@ size_t fwd_ws(tree_dtype dt, int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int6
     return use_mfma(dt, Hq, Hkv, D) ? mfma_fwd_ws_bytes((int)B, (int)N, (int)Hkv, (int)D) : 0;
 }
 
-size_t bwd_ws(tree_dtype, int64_t B, int64_t N, int64_t Hq, int64_t, int64_t) {
+size_t bwd_ws(tree_dtype dt, int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t D) {
+    if (use_mfma(dt, Hq, Hkv, D)) return mfma_bwd_ws_bytes((int)B, (int)N, (int)Hq, (int)Hkv, (int)D);
     return align_up((size_t)B * Hq * N * sizeof(float));  // delta
 }
 
@@ -90,5 +91,9 @@ extern "C" tree_status tree_attn_bwd(tree_dtype dt, const void* q, const void* k
     if (ws_bytes < need || !ws) return fail(TREE_ERR_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
     AttnArgs a{dt, q, k, v, subtree_end, (int)B, (int)N, (int)Hq, (int)Hkv, (int)D, softmax_scale,
                const_cast<void*>(out), const_cast<float*>(lse), dout, dq, dk, dv};
+    if (use_mfma(dt, Hq, Hkv, D))
+        return device_status(
+            mfma_attn_bwd(a, carve_bwd_ws(ws, (int)B, (int)N, (int)Hq, (int)Hkv, (int)D), (hipStream_t)stream),
+            "tree_attn_bwd launch");
     return device_status(vec_attn_bwd(a, (float*)ws, (hipStream_t)stream), "tree_attn_bwd launch");
 }

@@ -24,8 +24,21 @@ struct FwdWorkspace {
     uint16_t* vt;        // bf16 bits [B, Hkv, D, T*KT], keys permuted inside each 16-key group
 };
 
+// Workspace carved by the backward.
+struct BwdWorkspace {
+    float* delta;        // [B, Hq, N]  rowsum(dout * out)
+    uint16_t* qt;        // bf16 bits [B, Hq, D, T*KT]  Q^T, rows permuted in 16-row groups
+    uint16_t* dot;       // bf16 bits [B, Hq, D, T*KT]  dout^T, same layout
+    uint16_t* kt;        // bf16 bits [B, Hkv, D, T*KT] K^T, same layout
+    int32_t* tile_min;   // [B, T]
+    int32_t* tile_max;   // [B, T]
+};
+
 size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D);
 FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D);
 hipError_t mfma_attn_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st);
+size_t mfma_bwd_ws_bytes(int B, int N, int Hq, int Hkv, int D);
+BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D);
+hipError_t mfma_attn_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st);
 
 }  // namespace treeattn

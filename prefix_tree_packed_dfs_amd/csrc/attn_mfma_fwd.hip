@@ -28,21 +28,13 @@
 #include <climits>
 
 #include "attn_mfma.h"
-#include "device.h"
+#include "mfma_common.h"
 
 namespace treeattn {
 
 namespace {
 
 constexpr float kLn2 = 0.69314718055994531f;
-
-// Physical position of key k (0..15) inside its 16-key group of V^T: lane half
-// h reads keys {4h..4h+3, 8+4h..8+4h+3} as 8 contiguous values.
-__device__ __forceinline__ int inv_phys16(int w) { return ((w & 7) >> 2) * 8 + (w >> 3) * 4 + (w & 3); }
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // V -> V^T (keys permuted inside 16-key groups, zero past N) and per-tile
 // subtree_end range.  grid (T, Hkv, B), 256 threads.
@@ -83,19 +75,6 @@ __global__ __launch_bounds__(256) void fwd_prep(const __bf16* __restrict__ v, co
             tmax[(int64_t)b * T + t] = mx;
         }
     }
-}
-
-// First tile index >= from (and <= t_last) whose largest subtree_end reaches i0; -1 if none.
-// Wave-uniform: 64 tiles are tested per step with one ballot.
-__device__ __forceinline__ int next_visible(const int32_t* __restrict__ tmaxb, int from, int t_last, int i0) {
-    const int lane = threadIdx.x & 63;
-    for (int base = from; base <= t_last; base += 64) {
-        const int t = base + lane;
-        const bool vis = t <= t_last && tmaxb[t] >= i0;
-        const unsigned long long m = __ballot(vis);
-        if (m) return base + __ffsll((long long)m) - 1;
-    }
-    return -1;
 }
 
 template <int D, int HB>

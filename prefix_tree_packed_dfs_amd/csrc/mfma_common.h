@@ -1,0 +1,49 @@
+// Device helpers shared by the matrix-core kernels.
+//
+// Lane layouts of v_mfma_f32_32x32x16_bf16 (checked on gfx950 with an
+// in-bounds probe): for C = A B with A 32x16 and B 16x32,
+//   A: lane l, slot i holds A[l % 32][(l / 32) * 8 + i]
+//   B: lane l, slot i holds B[(l / 32) * 8 + i][l % 32]
+//   C: lane l, reg r  holds C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
+// so a lane of the accumulator owns one column and 16 rows: rows
+// {8j + 4h + (0..3)} for j = 0..3, h = l / 32.  Registers 8c..8c+7 of an
+// accumulator are therefore a valid B (or A-transposed) operand for the
+// 16-row chunk c of the next product, provided the other operand lists those
+// 16 rows in the same order: row m of the chunk is stored at position
+// phys16(m), which puts lane half h's eight rows next to each other.
+#pragma once
+
+#include "device.h"
+
+namespace treeattn {
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Position of row m (0..15) of a 16-row chunk in the permuted layout, and back.
+__device__ __forceinline__ int phys16(int m) { return ((m >> 2) & 1) * 8 + (m >> 3) * 4 + (m & 3); }
+__device__ __forceinline__ int inv_phys16(int w) { return ((w & 7) >> 2) * 8 + (w >> 3) * 4 + (w & 3); }
+
+// Row of accumulator register r for lane half h.
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+__device__ __forceinline__ void zero(f32x16& x) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = 0.f;
+}
+
+// First tile index >= from (and <= t_last) whose largest subtree_end reaches
+// i0; -1 if none.  Wave-uniform: 64 tiles are tested per step with one ballot.
+__device__ __forceinline__ int next_visible(const int32_t* __restrict__ tmaxb, int from, int t_last, int i0) {
+    const int lane = threadIdx.x & 63;
+    for (int base = from; base <= t_last; base += 64) {
+        const int t = base + lane;
+        const bool vis = t <= t_last && tmaxb[t] >= i0;
+        const unsigned long long m = __ballot(vis);
+        if (m) return base + __ffsll((long long)m) - 1;
+    }
+    return -1;
+}
+
+}  // namespace treeattn
