@@ -78,29 +78,33 @@ __global__ __launch_bounds__(256) void fwd_prep(const __bf16* __restrict__ v, co
 }
 
 template <int D, int HB>
-__global__ __launch_bounds__(256, 1) void fwd_main(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+__global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                    const __bf16* __restrict__ vt, const int32_t* __restrict__ se,
                                                    const int32_t* __restrict__ tmin,
                                                    const int32_t* __restrict__ tmax, int B, int N, int Hq,
                                                    int Hkv, int T, int n_qtiles, int n_chunks, float scale_log2,
                                                    __bf16* __restrict__ out, float* __restrict__ lse) {
-    constexpr int BM = 256 / HB;        // positions per workgroup
-    constexpr int NC = D / 16;          // 16-wide chunks of the head dim
-    constexpr int NDB = D / 32;         // 32-row blocks of the head dim
-    constexpr int KSTR = D * 2 + 16;    // LDS bytes per K row (padded: conflict-free b128 reads)
-    constexpr int VSTR = KT * 2 + 16;   // LDS bytes per V^T row
-    constexpr int KBYTES = KT * KSTR;
-    constexpr int VBYTES = D * VSTR;
-    constexpr int KCH = KT * D / 8 / 256;  // 16-byte chunks per thread per K tile
-    constexpr int VCH = D * KT / 8 / 256;  // ... per V^T tile
-    __shared__ __attribute__((aligned(16))) char smem[2 * (KBYTES + VBYTES)];
-    __shared__ int se_s[2][KT];
+    constexpr int BM = 256 / HB;          // positions per workgroup (8 waves x 32 rows = BM x HB)
+    constexpr int NC = D / 16;            // 16-wide chunks of the head dim
+    constexpr int NDB = D / 32;           // 32-row blocks of the head dim
+    constexpr int CPR = D / 8;            // 16-byte chunks per K row
+    constexpr int KROW = D * 2;           // LDS bytes per K row (16-byte chunks XOR-swizzled by row)
+    constexpr int KBYTES = KT * KROW;
+    constexpr int VROW = KT * 2;          // LDS bytes per V^T row (8 chunks, swizzled by row)
+    constexpr int VBYTES = D * VROW;
+    constexpr int STAGE = KBYTES + VBYTES + KT * 4;
+    constexpr int NSTAGE = 3;
+    constexpr int KDMA = KBYTES / 1024 / 8;   // 1 KB loads per wave per K tile
+    constexpr int VDMA = VBYTES / 1024 / 8;
+    constexpr int PER_TILE = KDMA + VDMA + 1; // vector memory ops per wave per tile
+    constexpr int LCAP = 1024;                // visible tiles listed per pass
+    constexpr int FULL = 1 << 30;
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+    __shared__ int list[LCAP];
+    __shared__ int list_meta[2];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
-
-    // work item: consecutive blocks go to different XCDs; the head-group index
-    // is the fast one so each XCD keeps to a fixed set of KV heads
     const int GH = B * Hkv * n_chunks;
     const int gi = blockIdx.x % GH;
     const int qi = blockIdx.x / GH;
@@ -109,191 +113,186 @@ __global__ __launch_bounds__(256, 1) void fwd_main(const __bf16* __restrict__ q,
     const int g = (gi / n_chunks) % Hkv;
     const int b = gi / (n_chunks * Hkv);
     const int G = Hq / Hkv;
-    const int head_base = g * G + chunk * HB;
+    const int head = g * G + chunk * HB + wave % HB;
     const int i0 = qt * BM;
     const int i_last = min(i0 + BM, N) - 1;
     const int t_last = i_last / KT;
     const int32_t* tmaxb = tmax + (int64_t)b * T;
     const int32_t* tminb = tmin + (int64_t)b * T;
     const int32_t* seb = se + (int64_t)b * N;
+    const int posb = i0 + (wave / HB) * 32;
+    const int ip = posb + l32;  // this lane's query position
 
-    int posb[2], head[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int bi = 2 * wave + qb;
-        head[qb] = head_base + bi % HB;
-        posb[qb] = i0 + (bi / HB) * 32;
-    }
-    bf16x8 qf[2][NC];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int p = posb[qb] + l32;
-        const __bf16* src = q + (((int64_t)b * N + p) * Hq + head[qb]) * D + hi * 8;
+    bf16x8 qf[NC];
+    {
+        const __bf16* src = q + (((int64_t)b * N + min(ip, N - 1)) * Hq + head) * D + hi * 8;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             bf16x8 z = {};
-            qf[qb][c] = p < N ? *reinterpret_cast<const bf16x8*>(src + 16 * c) : z;
+            qf[c] = ip < N ? *reinterpret_cast<const bf16x8*>(src + 16 * c) : z;
         }
     }
-    f32x16 acc[2][NDB];
+    f32x16 acc[NDB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.f;
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    for (int db = 0; db < NDB; ++db) zero(acc[db]);
+    float m_run = -INFINITY, l_run = 0.f;
 
     const int64_t vt_row = (int64_t)T * KT;
     const __bf16* vtb = vt + ((int64_t)b * Hkv + g) * D * vt_row;
-    bf16x8 rk[KCH], rv[VCH];
-    int rse = -1;
+    const __bf16* kb_ = k + ((int64_t)b * N * Hkv + g) * D;
 
-    auto load_tile = [&](int t) {
+    // all of this wave's loads of one tile: K rows (swizzled), V^T rows (swizzled), subtree_end
+    auto issue = [&](int t, int stage) {
+        char* dst = smem + stage * STAGE;
         const int j0 = t * KT;
 #pragma unroll
-        for (int u = 0; u < KCH; ++u) {
-            const int e = tid + 256 * u;
-            const int row = e / (D / 8), c = e % (D / 8), j = j0 + row;
-            bf16x8 z = {};
-            rk[u] = j < N ? *reinterpret_cast<const bf16x8*>(k + (((int64_t)b * N + j) * Hkv + g) * D + c * 8) : z;
+        for (int u = 0; u < KDMA; ++u) {
+            const int kk = wave * KDMA + u;  // which 1 KB of the K tile
+            const int row = kk * (64 / CPR) + lane / CPR;
+            const int gch = (lane % CPR) ^ (row % CPR);
+            const int j = min(j0 + row, N - 1);
+            dma16(kb_ + (int64_t)j * Hkv * D + gch * 8, dst + kk * 1024);
         }
 #pragma unroll
-        for (int u = 0; u < VCH; ++u) {
-            const int e = tid + 256 * u;
-            const int d = e / (KT / 8), c = e % (KT / 8);
-            rv[u] = *reinterpret_cast<const bf16x8*>(vtb + (int64_t)d * vt_row + j0 + c * 8);
+        for (int u = 0; u < VDMA; ++u) {
+            const int kk = wave * VDMA + u;
+            const int d = kk * 8 + lane / 8;
+            const int gsl = (lane % 8) ^ (d % 8);
+            dma16(vtb + (int64_t)d * vt_row + j0 + gsl * 8, dst + KBYTES + kk * 1024);
         }
-        if (tid < KT) rse = (j0 + tid < N) ? seb[j0 + tid] : -1;
-    };
-    auto store_tile = [&](int buf) {
-        char* kb = smem + buf * (KBYTES + VBYTES);
-        char* vb = kb + KBYTES;
-#pragma unroll
-        for (int u = 0; u < KCH; ++u) {
-            const int e = tid + 256 * u;
-            *reinterpret_cast<bf16x8*>(kb + (e / (D / 8)) * KSTR + (e % (D / 8)) * 16) = rk[u];
-        }
-#pragma unroll
-        for (int u = 0; u < VCH; ++u) {
-            const int e = tid + 256 * u;
-            *reinterpret_cast<bf16x8*>(vb + (e / (KT / 8)) * VSTR + (e % (KT / 8)) * 16) = rv[u];
-        }
-        if (tid < KT) se_s[buf][tid] = rse;
+        if (lane < 8) dma4(seb + min(j0 + wave * 8 + lane, N - 1), dst + KBYTES + VBYTES + wave * 32);
     };
 
-    int t = next_visible(tmaxb, 0, t_last, i0);
-    int cur = 0;
-    if (t >= 0) {
-        load_tile(t);
-        store_tile(0);
-    }
-    __syncthreads();
-    while (t >= 0) {
-        const int tn = next_visible(tmaxb, t + 1, t_last, i0);
-        if (tn >= 0) load_tile(tn);
-        const int j0 = t * KT;
-        const bool full = (j0 + KT - 1 <= i0) && (tminb[t] >= i_last);
-        const char* kb = smem + cur * (KBYTES + VBYTES);
-        const char* vb = kb + KBYTES;
-
-        // S^T = K Q^T for 64 keys x 64 queries
-        f32x16 s[2][2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[x][qb][r] = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + (x * 32 + l32) * KSTR + (hi * 8 + 16 * c) * 2);
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) s[x][qb] = mfma32(a, qf[qb][c], s[x][qb]);
+    int resume = 0;
+    while (resume >= 0) {
+        // visible tiles of this query block, in order, with their class
+        if (wave == 0) {
+            int cnt = 0, next = -1;
+            for (int base = resume; base <= t_last; base += 64) {
+                const int t = base + lane;
+                const bool vis = t <= t_last && tmaxb[t] >= i0;
+                const bool full = vis && (t * KT + KT - 1 <= i0) && tminb[t] >= i_last;
+                const unsigned long long m = __ballot(vis);
+                const int n_m = __popcll(m);
+                if (cnt + n_m > LCAP) {
+                    next = base;
+                    break;
+                }
+                const int pos = cnt + __popcll(m & ((1ull << lane) - 1ull));
+                if (vis) list[pos] = t | (full ? FULL : 0);
+                cnt += n_m;
+            }
+            if (lane == 0) {
+                list_meta[0] = cnt;
+                list_meta[1] = next;
             }
         }
-        if (!full) {
+        __syncthreads();
+        const int cnt = list_meta[0];
+        resume = list_meta[1];
+
+        if (cnt > 0) issue(list[0] & (FULL - 1), 0);
+        if (cnt > 1) issue(list[1] & (FULL - 1), 1);
+        for (int it = 0; it < cnt; ++it) {
+            if (it + 1 < cnt) wait_vmcnt<PER_TILE>();
+            else wait_vmcnt<0>();
+            barrier();
+            if (it + 2 < cnt) issue(list[it + 2] & (FULL - 1), (it + 2) % NSTAGE);
+            const int e = list[it];
+            const int t = e & (FULL - 1);
+            const bool full = (e & FULL) != 0;
+            const int j0 = t * KT;
+            const char* st = smem + (it % NSTAGE) * STAGE;
+
+            // S^T = K Q^T: 64 keys x this wave's 32 queries
+            f32x16 sacc[2];
+            zero(sacc[0]);
+            zero(sacc[1]);
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+            for (int c = 0; c < NC; ++c)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int jj = x * 32 + 8 * (r >> 2) + hi * 4 + (r & 3);
-                    const int j = j0 + jj, sej = se_s[cur][jj];
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) {
-                        const int ip = posb[qb] + l32;
-                        if (!(j <= ip && ip <= sej)) s[x][qb][r] = -INFINITY;
-                    }
+                for (int x = 0; x < 2; ++x) {
+                    const int row = x * 32 + l32;
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        st + row * KROW + (((hi + 2 * c) ^ (row % CPR)) * 16));
+                    sacc[x] = mfma32(a, qf[c], sacc[x]);
                 }
-        }
-        // online softmax per query (one query per lane per block)
-        bf16x8 pf[2][2][2];
+            if (!full) {
+                const int* ses = reinterpret_cast<const int*>(st + KBYTES + VBYTES);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int jj = x * 32 + 8 * gq + 4 * hi;
+                        const int4 s4 = *reinterpret_cast<const int4*>(ses + jj);
+                        const int sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+                        for (int e4 = 0; e4 < 4; ++e4)
+                            if (!(j0 + jj + e4 <= ip && ip <= sv[e4])) sacc[x][gq * 4 + e4] = -INFINITY;
+                    }
+            }
+            // online softmax; the running max is only raised (and the output
+            // rescaled) when a new score exceeds it by more than 2^8
             float mx = -INFINITY;
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[x][qb][r]);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[x][r]);
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run[qb], mx * scale_log2);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float corr = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
-            m_run[qb] = m_new;
+            const float mxs = mx * scale_log2;
+            if (__ballot(mxs > m_run + 8.f)) {
+                const float m_new = fmaxf(m_run, mxs);
+                const float corr = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= corr;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[db][r] *= corr;
+                m_run = m_new;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            bf16x8 pf[2][2];
             float rs = 0.f;
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[x][qb][r], scale_log2, -m_use));
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[x][r], scale_log2, -m_use));
                     rs += p;
-                    pf[qb][x][r >> 3][r & 7] = (__bf16)p;
+                    pf[x][r >> 3][r & 7] = (__bf16)p;
                 }
-            l_run[qb] = l_run[qb] * corr + rs;
+            l_run += rs;
+            // O^T += V^T P^T
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[qb][db][r] *= corr;
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int c2 = 0; c2 < 2; ++c2) {
+                        const int d = db * 32 + l32;
+                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                            st + KBYTES + d * VROW + (((x * 4 + c2 * 2 + hi) ^ (d % 8)) * 16));
+                        acc[db] = mfma32(a, pf[x][c2], acc[db]);
+                    }
         }
-        // O^T += V^T P^T
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int x = 0; x < 2; ++x)
-#pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + (db * 32 + l32) * VSTR +
-                                                                      (x * 32 + c2 * 16 + hi * 8) * 2);
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) acc[qb][db] = mfma32(a, pf[qb][x][c2], acc[qb][db]);
-                }
-        if (tn >= 0) store_tile(cur ^ 1);
-        __syncthreads();
-        cur ^= 1;
-        t = tn;
+        __syncthreads();  // the list is rebuilt only after every wave is done with it
     }
 
     // epilogue: O = O^T / l, lse = (m + log2 l) ln 2
+    const float lt = l_run + __shfl_xor(l_run, 32, 64);
+    if (ip < N) {
+        const float inv = 1.f / lt;
+        __bf16* o = out + (((int64_t)b * N + ip) * Hq + head) * D;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
-        const int p = posb[qb] + l32;
-        if (p < N) {
-            const float inv = 1.f / lt;
-            __bf16* o = out + (((int64_t)b * N + p) * Hq + head[qb]) * D;
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+            for (int grp = 0; grp < 4; ++grp) {
+                bf16x4 v4;
 #pragma unroll
-                for (int grp = 0; grp < 4; ++grp) {
-                    bf16x4 v4;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[qb][db][grp * 4 + e] * inv);
-                    *reinterpret_cast<bf16x4*>(o + db * 32 + grp * 8 + hi * 4) = v4;
-                }
-            if (hi == 0) lse[((int64_t)b * Hq + head[qb]) * N + p] = (m_run[qb] + __log2f(lt)) * kLn2;
-        }
+                for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[db][grp * 4 + e] * inv);
+                *reinterpret_cast<bf16x4*>(o + db * 32 + grp * 8 + hi * 4) = v4;
+            }
+        if (hi == 0) lse[((int64_t)b * Hq + head) * N + ip] = (m_run + __log2f(lt)) * kLn2;
     }
 }
 
@@ -305,7 +304,7 @@ hipError_t launch_main(const AttnArgs& a, const FwdWorkspace& w, int T, hipStrea
     const int n_qtiles = (a.N + BM - 1) / BM;
     const int64_t blocks = (int64_t)n_qtiles * a.B * a.Hkv * n_chunks;
     const float scale_log2 = a.scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((fwd_main<D, HB>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)a.q,
+    hipLaunchKernelGGL((fwd_main<D, HB>), dim3((unsigned)blocks), dim3(512), 0, st, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)w.vt, a.se, w.tile_min, w.tile_max, a.B, a.N, a.Hq,
                        a.Hkv, T, n_qtiles, n_chunks, scale_log2, (__bf16*)a.out, a.lse);
     return hipGetLastError();

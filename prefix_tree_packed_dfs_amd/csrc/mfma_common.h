@@ -46,4 +46,36 @@ __device__ __forceinline__ int next_visible(const int32_t* __restrict__ tmaxb, i
     return -1;
 }
 
+// ---------------------------------------------------------------------------
+// Direct global -> LDS loads and explicit synchronisation.
+//
+// global_load_lds_dwordx4 writes lane i's 16 bytes to LDS at base + 16 * i
+// (base is wave-uniform), so one instruction fills 1 KB of LDS and needs no
+// registers.  The loads are tracked by vmcnt, which counts in issue order:
+// wait_vmcnt<n>() returns once at most n of this wave's vector memory
+// operations are still in flight.  __syncthreads() would wait for all of
+// them (vmcnt(0)); barrier() does not, so prefetches of later tiles stay in
+// flight across it.  Every wave must wait for its own loads before the
+// barrier that publishes them.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glob_void_t;
+
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((glob_void_t*)gsrc, (lds_void_t*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((glob_void_t*)gsrc, (lds_void_t*)lds_base, 4, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt low bits [3:0], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0xF70 | N);
+}
+
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 }  // namespace treeattn
