@@ -32,7 +32,18 @@ struct BwdWorkspace {
     uint16_t* kt;        // bf16 bits [B, Hkv, D, T*KT] K^T, same layout
     int32_t* tile_min;   // [B, T]
     int32_t* tile_max;   // [B, T]
+    // dK/dV work plan: KV tiles of 256 keys whose query range is long are split
+    // into chunks of visits; chunks write fp32 partials that a reduce pass sums
+    int32_t* ctrl;       // queue counters / lengths / starts, split-tile count
+    int4* tile_plan;     // [B * T256] {visits, splits, compact index, first slot}
+    int4* units;         // [unit capacity][2] {b*Hkv+g, tile, first visit, end visit}, {slot, 0, 0, 0}
+    int4* split_tiles;   // [kSplitSlots/2] {b, tile, first slot, splits}
+    float* partial;      // [kSplitSlots][2][256][D] fp32 dK, dV partial sums
 };
+
+// Partial-sum slots for split dK/dV tiles, and the initial visit budget per chunk.
+constexpr int kSplitSlots = 768;
+constexpr int kVisitBudget = 96;
 
 size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D);
 FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D);

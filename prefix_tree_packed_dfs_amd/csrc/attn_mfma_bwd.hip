@@ -38,6 +38,19 @@ __device__ __forceinline__ T ld16(const void* p) {
     return *reinterpret_cast<const T*>(p);
 }
 
+// Compute units of the current device (cached per device).
+int num_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 // grid (T, Hq, B), 256 threads
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -129,36 +142,203 @@ __global__ __launch_bounds__(256) void bwd_prep(const __bf16* __restrict__ q, co
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: grid (ceil(N/128) * B * Hkv), 256 threads
+// dK/dV work plan (one workgroup).  A KV tile of 256 keys visits every
+// (32-position block, query head) pair from its first key to the largest
+// subtree_end among its keys.  Keys of a long shared prefix visit almost the
+// whole row while keys near the leaves visit a few blocks, so tiles whose
+// visit count exceeds the budget are split into chunks; the budget doubles
+// until the chunks fit the partial-sum slots.  Units are queued per KV head
+// group (g mod NQ, so one XCD keeps one head's data in its L2), split chunks
+// first, then whole tiles.
+// ctrl: [0..7] queue counters, [8..15] lengths, [16..23] starts, [24] split tiles.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tmax, int B, int N, int T, int G,
+                                                 int Hkv, int* __restrict__ ctrl, int4* __restrict__ tile_plan,
+                                                 int4* __restrict__ units, int4* __restrict__ split_tiles) {
+    __shared__ int s_sum, s_budget, s_tot[3];
+    const int tid = threadIdx.x;
+    const int T256 = (N + 255) / 256;
+    const int BT = B * T256;
+    const int NQ = Hkv < 8 ? Hkv : 8;
+    for (int u = tid; u < BT; u += 1024) {
+        const int b = u / T256, t = u % T256;
+        int qmax = -1;
+        for (int x = 4 * t; x < min(4 * t + 4, T); ++x) qmax = max(qmax, tmax[(int64_t)b * T + x]);
+        const int nv = (qmax / 32 - (t * 256) / 32 + 1) * G;
+        tile_plan[u] = make_int4(nv, 1, 0, 0);
+    }
+    if (tid == 0) s_budget = kVisitBudget;
+    __syncthreads();
+    for (;;) {
+        if (tid == 0) s_sum = 0;
+        __syncthreads();
+        const int budget = s_budget;
+        int part = 0;
+        for (int u = tid; u < BT; u += 1024) {
+            const int nv = tile_plan[u].x;
+            if (nv > budget) part += (nv + budget - 1) / budget;
+        }
+        if (part) atomicAdd(&s_sum, part);
+        __syncthreads();
+        const bool fits = (int64_t)s_sum * Hkv <= kSplitSlots;
+        __syncthreads();
+        if (fits) break;
+        if (tid == 0) s_budget = budget * 2;
+        __syncthreads();
+    }
+    const int budget = s_budget;
+    if (tid == 0) {  // compaction (sequential: one entry per 256-key tile of the batch)
+        int n_split = 0, n_single = 0, slot = 0;
+        for (int u = 0; u < BT; ++u) {
+            int4 e = tile_plan[u];
+            if (e.x > budget) {
+                e.y = (e.x + budget - 1) / budget;
+                e.z = n_split++;
+                e.w = slot;
+                slot += e.y;
+                split_tiles[e.z] = make_int4(u / T256, u % T256, e.w, e.y);
+            } else {
+                e.y = 1;
+                e.z = n_single++;
+                e.w = -1;
+            }
+            tile_plan[u] = e;
+        }
+        s_tot[0] = slot;       // chunks of split tiles (per head)
+        s_tot[1] = n_single;
+        s_tot[2] = n_split;
+        int start = 0;
+        for (int x = 0; x < NQ; ++x) {
+            const int hg = (Hkv - x + NQ - 1) / NQ;  // heads in queue x
+            ctrl[x] = 0;
+            ctrl[8 + x] = (slot + n_single) * hg;
+            ctrl[16 + x] = start;
+            start += (slot + n_single) * hg;
+        }
+        ctrl[24] = n_split;
+    }
+    __syncthreads();
+    const int chunks = s_tot[0];
+    for (int u = tid; u < BT; u += 1024) {
+        const int4 e = tile_plan[u];
+        const int b = u / T256, t = u % T256;
+        for (int g = 0; g < Hkv; ++g) {
+            const int x = g % NQ, r = g / NQ, hg = (Hkv - x + NQ - 1) / NQ;
+            const int qs = ctrl[16 + x];
+            if (e.w >= 0) {
+                const int per = (e.x + e.y - 1) / e.y;
+                for (int kk = 0; kk < e.y; ++kk) {
+                    const int idx = qs + (e.w + kk) * hg + r;
+                    units[2 * idx] = make_int4(b * Hkv + g, t, kk * per, min((kk + 1) * per, e.x));
+                    units[2 * idx + 1] = make_int4((e.w + kk) * Hkv + g, 0, 0, 0);
+                }
+            } else {
+                const int idx = qs + (chunks + e.z) * hg + r;
+                units[2 * idx] = make_int4(b * Hkv + g, t, 0, e.x);
+                units[2 * idx + 1] = make_int4(-1, 0, 0, 0);
+            }
+        }
+    }
+}
+
+// Sum the chunk partials of split tiles in chunk order and write bf16 dK, dV.
+// grid (kSplitSlots / 2 [an upper bound on split tiles x KV heads], 8 chunks
+// of 32 keys), 256 threads.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_reduce(const int* __restrict__ ctrl,
+                                                 const int4* __restrict__ split_tiles,
+                                                 const float* __restrict__ partial, int N, int Hkv,
+                                                 __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
+    const int w = blockIdx.x;
+    const int n_split = ctrl[24];
+    if (w >= n_split * Hkv) return;
+    const int4 st = split_tiles[w / Hkv];
+    const int g = w % Hkv;
+    const int b = st.x, j0 = st.y * 256;
+    const int k0 = blockIdx.y * 32;
+    constexpr int SLOT = 2 * 256 * D;  // floats per slot
+    for (int e = threadIdx.x; e < 2 * 32 * D / 4; e += 256) {
+        const int which = e / (32 * D / 4);           // 0: dK, 1: dV
+        const int rem = e % (32 * D / 4);
+        const int kl = k0 + rem / (D / 4), d4 = rem % (D / 4);
+        const int j = j0 + kl;
+        if (j >= N) continue;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int kk = 0; kk < st.w; ++kk) {
+            const float4 v = *reinterpret_cast<const float4*>(
+                partial + (int64_t)((st.z + kk) * Hkv + g) * SLOT + which * 256 * D + kl * D + d4 * 4);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        bf16x4 o;
+        o[0] = (__bf16)acc.x;
+        o[1] = (__bf16)acc.y;
+        o[2] = (__bf16)acc.z;
+        o[3] = (__bf16)acc.w;
+        __bf16* dst = (which ? dv : dk) + (((int64_t)b * N + j) * Hkv + g) * D + d4 * 4;
+        *reinterpret_cast<bf16x4*>(dst) = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: persistent, one 512-thread workgroup per CU (8 waves x 32 keys);
+// work units come from the plan's queues
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+__global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                    const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
                                                    const float* __restrict__ lse, const float* __restrict__ delta,
                                                    const __bf16* __restrict__ qt, const __bf16* __restrict__ dot,
                                                    const int32_t* __restrict__ se, int B, int N, int Hq, int Hkv,
-                                                   int T, float scale_log2, float scale, __bf16* __restrict__ dk,
-                                                   __bf16* __restrict__ dv) {
+                                                   int T, float scale_log2, float scale, int* __restrict__ ctrl,
+                                                   const int4* __restrict__ units, float* __restrict__ partial,
+                                                   __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
     constexpr int NC = D / 16, NDB = D / 32;
-    constexpr int RSTR = D * 2 + 16;     // LDS bytes per natural row (32 rows per block)
-    constexpr int TSTR = 32 * 2 + 16;    // LDS bytes per transposed row (32 positions)
-    constexpr int NBYTES = 32 * RSTR;
-    constexpr int TBYTES = D * TSTR;
-    constexpr int BUF = 2 * NBYTES + 2 * TBYTES;
-    constexpr int NCH = 32 * D / 8 / 256;  // 16-byte chunks per thread per natural tile
-    constexpr int TCH = D * 32 / 8 / 256;  // ... per transposed tile
-    __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
-    __shared__ float l2s[2][32], dls[2][32];
-    __shared__ int qmax_s[4];
+    constexpr int CPR = D / 8;             // 16-byte chunks per natural row
+    constexpr int NROW = D * 2;            // LDS bytes per natural row (32 rows per visit)
+    constexpr int NBYTES = 32 * NROW;
+    constexpr int TROW = 64;               // LDS bytes per transposed row (32 positions)
+    constexpr int TBYTES = D * TROW;
+    constexpr int STAGE = 2 * NBYTES + 2 * TBYTES + 256;
+    constexpr int NSTAGE = 4;
+    // 16-byte chunks each wave loads per tile; below 64 a single load with
+    // only the first lanes active (head dim 64)
+    constexpr int NCH = NBYTES / 16 / 8;
+    constexpr int TCH = TBYTES / 16 / 8;
+    constexpr int NDMA = NCH >= 64 ? NCH / 64 : 1;
+    constexpr int TDMA = TCH >= 64 ? TCH / 64 : 1;
+    constexpr int NLANES = NCH >= 64 ? 64 : NCH;
+    constexpr int TLANES = TCH >= 64 ? 64 : TCH;
+    constexpr int PER_VISIT = 2 * NDMA + 2 * TDMA + 1;
+    static_assert(NSTAGE == 4 && 2 * PER_VISIT < 16, "wait counts below assume four stages");
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+    __shared__ int qmax_s[8];
+    __shared__ int4 unit_s[2];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
-    const int GH = B * Hkv;
-    const int gi = blockIdx.x % GH;
-    const int kt_i = blockIdx.x / GH;  // ascending: keys early in the row have the longest query ranges
-    const int g = gi % Hkv, b = gi / Hkv;
     const int G = Hq / Hkv;
-    const int j0 = kt_i * 128;
+    const int NQ = Hkv < 8 ? Hkv : 8;
+    const int qx = blockIdx.x % NQ;
+    for (;;) {
+    if (tid == 0) {
+        const int idx = atomicAdd(&ctrl[qx], 1);
+        if (idx < ctrl[8 + qx]) {
+            unit_s[0] = units[2 * (ctrl[16 + qx] + idx)];
+            unit_s[1] = units[2 * (ctrl[16 + qx] + idx) + 1];
+        } else {
+            unit_s[0] = make_int4(-1, 0, 0, 0);
+        }
+    }
+    __syncthreads();
+    const int4 un = unit_s[0];
+    const int slot = unit_s[1].x;
+    if (un.x < 0) break;
+    const int g = un.x % Hkv, b = un.x / Hkv;
+    const int j0 = un.y * 256;
+    const int v_begin = un.z;
     const int j0w = j0 + 32 * wave;
     const int jk = j0w + l32;
     const bool kvalid = jk < N;
@@ -169,7 +349,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(const __bf16* __restrict__ q,
 
     bf16x8 kf[NC], vf[NC];
     {
-        const int64_t off = (((int64_t)b * N + jk) * Hkv + g) * D + hi * 8;
+        const int64_t off = (((int64_t)b * N + min(jk, N - 1)) * Hkv + g) * D + hi * 8;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             bf16x8 z = {};
@@ -185,112 +365,110 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(const __bf16* __restrict__ q,
     }
     if (lane == 0) qmax_s[wave] = wmax;
     __syncthreads();
-    const int qmax = max(max(qmax_s[0], qmax_s[1]), max(qmax_s[2], qmax_s[3]));
-    const int pb0 = j0 / 32, pb1 = qmax / 32;
-    const int nvis = (pb1 - pb0 + 1) * G;
+    int qmax = qmax_s[0];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) qmax = max(qmax, qmax_s[w]);
+    const int pb0 = j0 / 32;
+    const int nvis = un.w - un.z;  // this unit's visits [v_begin, v_end) of the tile
+    (void)qmax;
     const int64_t row_len = (int64_t)T * KT;
 
-    bf16x8 sq[NCH], sd[NCH], sqt[TCH], sdt[TCH];
-    float sl = 0.f, sdl = 0.f;
-    auto load_vis = [&](int vi) {
+    // all of this wave's loads for one visit (32 positions x one query head)
+    auto issue = [&](int vl, int stage) {
+        char* dst = smem + stage * STAGE;
+        const int vi = v_begin + vl;
         const int i0 = (pb0 + vi / G) * 32;
         const int h = g * G + vi % G;
 #pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int e = tid + 256 * u;
-            const int r = e / (D / 8), c = e % (D / 8), i = i0 + r;
-            const int64_t off = (((int64_t)b * N + i) * Hq + h) * D + c * 8;
-            bf16x8 z = {};
-            sq[u] = i < N ? ld16<bf16x8>(q + off) : z;
-            sd[u] = i < N ? ld16<bf16x8>(dout + off) : z;
+        for (int u = 0; u < NDMA; ++u) {
+            const int e0 = wave * NCH + u * 64;  // first chunk of this load
+            const int e = e0 + lane;
+            const int row = e / CPR;
+            const int gch = (e % CPR) ^ (row % CPR);
+            const int64_t off = (((int64_t)b * N + min(i0 + row, N - 1)) * Hq + h) * D + gch * 8;
+            if (lane < NLANES) {
+                dma16(q + off, dst + e0 * 16);
+                dma16(dout + off, dst + NBYTES + e0 * 16);
+            }
         }
+        const int64_t tbase = ((int64_t)b * Hq + h) * D * row_len + i0;
 #pragma unroll
-        for (int u = 0; u < TCH; ++u) {
-            const int e = tid + 256 * u;
-            const int d = e / 4, c = e % 4;
-            const int64_t off = ((int64_t)b * Hq + h) * D * row_len + (int64_t)d * row_len + i0 + c * 8;
-            sqt[u] = ld16<bf16x8>(qt + off);
-            sdt[u] = ld16<bf16x8>(dot + off);
+        for (int u = 0; u < TDMA; ++u) {
+            const int e0 = wave * TCH + u * 64;
+            const int e = e0 + lane;
+            const int d = e / 4;
+            const int gsl = (e % 4) ^ ((d >> 2) & 3);
+            const int64_t off = tbase + (int64_t)d * row_len + gsl * 8;
+            if (lane < TLANES) {
+                dma16(qt + off, dst + 2 * NBYTES + e0 * 16);
+                dma16(dot + off, dst + 2 * NBYTES + TBYTES + e0 * 16);
+            }
         }
-        if (tid < 32) {
-            const int i = i0 + tid;
-            sl = i < N ? lse[((int64_t)b * Hq + h) * N + i] * kLog2e : 0.f;
-            sdl = i < N ? delta[((int64_t)b * Hq + h) * N + i] : 0.f;
-        }
-    };
-    auto store_vis = [&](int buf) {
-        char* qn = smem + buf * BUF;
-        char* dn = qn + NBYTES;
-        char* qtt = dn + NBYTES;
-        char* dtt = qtt + TBYTES;
-#pragma unroll
-        for (int u = 0; u < NCH; ++u) {
-            const int e = tid + 256 * u;
-            const int o = (e / (D / 8)) * RSTR + (e % (D / 8)) * 16;
-            *reinterpret_cast<bf16x8*>(qn + o) = sq[u];
-            *reinterpret_cast<bf16x8*>(dn + o) = sd[u];
-        }
-#pragma unroll
-        for (int u = 0; u < TCH; ++u) {
-            const int e = tid + 256 * u;
-            const int o = (e / 4) * TSTR + (e % 4) * 16;
-            *reinterpret_cast<bf16x8*>(qtt + o) = sqt[u];
-            *reinterpret_cast<bf16x8*>(dtt + o) = sdt[u];
-        }
-        if (tid < 32) {
-            l2s[buf][tid] = sl;
-            dls[buf][tid] = sdl;
+        if (lane < 8) {
+            const int64_t roff = ((int64_t)b * Hq + h) * N + min(i0 + (wave & 3) * 8 + lane, N - 1);
+            dma4((wave < 4 ? lse : delta) + roff, dst + 2 * NBYTES + 2 * TBYTES + wave * 32);
         }
     };
 
-    load_vis(0);
-    store_vis(0);
-    __syncthreads();
-    int cur = 0;
+#pragma unroll
+    for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
+        if (s0 < nvis) issue(s0, s0);
     for (int vi = 0; vi < nvis; ++vi) {
-        if (vi + 1 < nvis) load_vis(vi + 1);
-        const int i_lo = (pb0 + vi / G) * 32;
+        // visits issued after this one and possibly still in flight
+        const int ahead = min(nvis - 1 - vi, NSTAGE - 2);
+        if (ahead >= 2) wait_vmcnt<2 * PER_VISIT>();
+        else if (ahead == 1) wait_vmcnt<PER_VISIT>();
+        else wait_vmcnt<0>();
+        barrier();
+        if (vi + NSTAGE - 1 < nvis) issue(vi + NSTAGE - 1, (vi + NSTAGE - 1) % NSTAGE);
+        const int i_lo = (pb0 + (v_begin + vi) / G) * 32;
         const bool skip = (j0w > i_lo + 31) || (wmax < i_lo);
-        if (!skip) {
-            const bool full = (j0w + 31 <= i_lo) && (wmin >= i_lo + 31);
-            const char* qn = smem + cur * BUF;
-            const char* dn = qn + NBYTES;
-            const char* qtt = dn + NBYTES;
-            const char* dtt = qtt + TBYTES;
-            f32x16 s, dp;
-            zero(s);
-            zero(dp);
+        if (skip) continue;
+        const bool full = (j0w + 31 <= i_lo) && (wmin >= i_lo + 31);
+        const char* st = smem + (vi % NSTAGE) * STAGE;
+        const char* tq = st + 2 * NBYTES;
+        const char* td = tq + TBYTES;
+        const float* l2s = reinterpret_cast<const float*>(td + TBYTES);
+        const float* dls = l2s + 32;
+        // S = Q K^T, dP = dout V^T: 32 queries x this wave's 32 keys
+        f32x16 s, dp;
+        zero(s);
+        zero(dp);
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const int o = l32 * RSTR + (hi * 8 + 16 * c) * 2;
-                s = mfma32(ld16<bf16x8>(qn + o), kf[c], s);
-                dp = mfma32(ld16<bf16x8>(dn + o), vf[c], dp);
-            }
-            bf16x8 pbf[2], dsf[2];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = acc_row(r, hi);
-                const int i = i_lo + m;
-                float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -l2s[cur][m]));
-                if (!full && !(jk <= i && i <= sek)) p = 0.f;
-                const float ds = p * (dp[r] - dls[cur][m]);
-                pbf[r >> 3][r & 7] = (__bf16)p;
-                dsf[r >> 3][r & 7] = (__bf16)ds;
-            }
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    const int o = (db * 32 + l32) * TSTR + (c2 * 16 + hi * 8) * 2;
-                    dvt[db] = mfma32(ld16<bf16x8>(dtt + o), pbf[c2], dvt[db]);
-                    dkt[db] = mfma32(ld16<bf16x8>(qtt + o), dsf[c2], dkt[db]);
-                }
+        for (int c = 0; c < NC; ++c) {
+            const int o = l32 * NROW + (((hi + 2 * c) ^ (l32 % CPR)) * 16);
+            s = mfma32(ld16<bf16x8>(st + o), kf[c], s);
+            dp = mfma32(ld16<bf16x8>(st + NBYTES + o), vf[c], dp);
         }
-        if (vi + 1 < nvis) store_vis(cur ^ 1);
-        __syncthreads();
-        cur ^= 1;
+        bf16x8 pbf[2], dsf[2];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int m0 = 8 * gq + 4 * hi;
+            const float4 l4 = *reinterpret_cast<const float4*>(l2s + m0);
+            const float4 d4 = *reinterpret_cast<const float4*>(dls + m0);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = gq * 4 + e;
+                const int i = i_lo + m0 + e;
+                float p = __builtin_amdgcn_exp2f(s[r] * scale_log2 - lv[e] * kLog2e);
+                if (!full && !(jk <= i && i <= sek)) p = 0.f;
+                pbf[r >> 3][r & 7] = (__bf16)p;
+                dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl[e]));
+            }
+        }
+        // dV^T += dout^T P, dK^T += Q^T dS
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const int d = db * 32 + l32;
+                const int o = d * TROW + (((c2 * 2 + hi) ^ ((d >> 2) & 3)) * 16);
+                dvt[db] = mfma32(ld16<bf16x8>(td + o), pbf[c2], dvt[db]);
+                dkt[db] = mfma32(ld16<bf16x8>(tq + o), dsf[c2], dkt[db]);
+            }
     }
-    if (kvalid) {
+    if (kvalid && slot < 0) {
         __bf16* okp = dk + (((int64_t)b * N + jk) * Hkv + g) * D;
         __bf16* ovp = dv + (((int64_t)b * N + jk) * Hkv + g) * D;
 #pragma unroll
@@ -306,15 +484,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(const __bf16* __restrict__ q,
                 *reinterpret_cast<bf16x4*>(okp + db * 32 + grp * 8 + hi * 4) = a4;
                 *reinterpret_cast<bf16x4*>(ovp + db * 32 + grp * 8 + hi * 4) = b4;
             }
+    } else if (slot >= 0) {  // a chunk of a split tile: fp32 partials, summed by bwd_reduce
+        float* pk = partial + (int64_t)slot * 2 * 256 * D + (32 * wave + l32) * D;
+        float* pv = pk + 256 * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                const int d = db * 32 + grp * 8 + hi * 4;
+                *reinterpret_cast<float4*>(pk + d) =
+                    make_float4(dkt[db][grp * 4] * scale, dkt[db][grp * 4 + 1] * scale,
+                                dkt[db][grp * 4 + 2] * scale, dkt[db][grp * 4 + 3] * scale);
+                *reinterpret_cast<float4*>(pv + d) =
+                    make_float4(dvt[db][grp * 4], dvt[db][grp * 4 + 1], dvt[db][grp * 4 + 2], dvt[db][grp * 4 + 3]);
+            }
+    }
+    __syncthreads();  // unit_s and qmax_s are reused by the next unit
     }
 }
 
 // ---------------------------------------------------------------------------
-// dQ: grid (n_qtiles * B * Hkv * n_chunks), 256 threads; same work split as
-// the forward (BM positions x HB heads per workgroup, 64 rows per wave).
+// dQ: grid (n_qtiles * B * Hkv * n_chunks), 512 threads; same work split as
+// the forward (BM positions x HB heads per workgroup, 32 rows per wave).
 // ---------------------------------------------------------------------------
 template <int D, int HB>
-__global__ __launch_bounds__(256, 1) void bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+__global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                  const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
                                                  const float* __restrict__ lse, const float* __restrict__ delta,
                                                  const __bf16* __restrict__ ktr, const int32_t* __restrict__ se,
@@ -323,15 +517,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(const __bf16* __restrict__ q, c
                                                  float scale_log2, float scale, __bf16* __restrict__ dq) {
     constexpr int BM = 256 / HB;
     constexpr int NC = D / 16, NDB = D / 32;
-    constexpr int KSTR = D * 2 + 16;     // natural K / V rows
-    constexpr int TSTR = KT * 2 + 16;    // K^T rows
-    constexpr int KBYTES = KT * KSTR;
-    constexpr int TBYTES = D * TSTR;
-    constexpr int BUF = 2 * KBYTES + TBYTES;
-    constexpr int KCH = KT * D / 8 / 256;
-    constexpr int TCH = D * KT / 8 / 256;
-    __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
-    __shared__ int se_s[2][KT];
+    constexpr int CPR = D / 8;
+    constexpr int KROW = D * 2;            // natural K / V rows, swizzled
+    constexpr int KBYTES = KT * KROW;
+    constexpr int TROW = KT * 2;           // K^T rows, swizzled
+    constexpr int TBYTES = D * TROW;
+    constexpr int STAGE = 2 * KBYTES + TBYTES + KT * 4;
+    constexpr int NSTAGE = 3;
+    constexpr int KDMA = KBYTES / 1024 / 8;
+    constexpr int TDMA = TBYTES / 1024 / 8;
+    constexpr int PER_TILE = 2 * KDMA + TDMA + 1;
+    constexpr int LCAP = 1024;
+    constexpr int FULL = 1 << 30;
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+    __shared__ int list[LCAP];
+    __shared__ int list_meta[2];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -343,155 +543,155 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(const __bf16* __restrict__ q, c
     const int g = (gi / n_chunks) % Hkv;
     const int b = gi / (n_chunks * Hkv);
     const int G = Hq / Hkv;
-    const int head_base = g * G + chunk * HB;
+    const int head = g * G + chunk * HB + wave % HB;
     const int i0 = qtile * BM;
     const int i_last = min(i0 + BM, N) - 1;
     const int t_last = i_last / KT;
     const int32_t* tmaxb = tmax + (int64_t)b * T;
     const int32_t* tminb = tmin + (int64_t)b * T;
     const int32_t* seb = se + (int64_t)b * N;
+    const int ip = i0 + (wave / HB) * 32 + l32;
 
-    int posb[2], head[2];
-    bf16x8 qf[2][NC], df[2][NC];
-    float l2q[2], dlq[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int bi = 2 * wave + qb;
-        head[qb] = head_base + bi % HB;
-        posb[qb] = i0 + (bi / HB) * 32;
-        const int p = posb[qb] + l32;
-        const int64_t off = (((int64_t)b * N + p) * Hq + head[qb]) * D + hi * 8;
+    bf16x8 qf[NC], df[NC];
+    float l2q, dlq;
+    {
+        const int pc = min(ip, N - 1);
+        const int64_t off = (((int64_t)b * N + pc) * Hq + head) * D + hi * 8;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             bf16x8 z = {};
-            qf[qb][c] = p < N ? ld16<bf16x8>(q + off + 16 * c) : z;
-            df[qb][c] = p < N ? ld16<bf16x8>(dout + off + 16 * c) : z;
+            qf[c] = ip < N ? ld16<bf16x8>(q + off + 16 * c) : z;
+            df[c] = ip < N ? ld16<bf16x8>(dout + off + 16 * c) : z;
         }
-        l2q[qb] = p < N ? lse[((int64_t)b * Hq + head[qb]) * N + p] * kLog2e : 0.f;
-        dlq[qb] = p < N ? delta[((int64_t)b * Hq + head[qb]) * N + p] : 0.f;
+        l2q = ip < N ? lse[((int64_t)b * Hq + head) * N + pc] * kLog2e : 0.f;
+        dlq = ip < N ? delta[((int64_t)b * Hq + head) * N + pc] : 0.f;
     }
-    f32x16 acc[2][NDB];
+    f32x16 acc[NDB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) zero(acc[qb][db]);
+    for (int db = 0; db < NDB; ++db) zero(acc[db]);
 
     const int64_t row_len = (int64_t)T * KT;
     const __bf16* ktb = ktr + ((int64_t)b * Hkv + g) * D * row_len;
-    bf16x8 rk[KCH], rv[KCH], rt[TCH];
-    int rse = -1;
-    auto load_tile = [&](int t) {
+    const int64_t kvbase = ((int64_t)b * N * Hkv + g) * D;
+
+    auto issue = [&](int t, int stage) {
+        char* dst = smem + stage * STAGE;
         const int j0 = t * KT;
 #pragma unroll
-        for (int u = 0; u < KCH; ++u) {
-            const int e = tid + 256 * u;
-            const int row = e / (D / 8), c = e % (D / 8), j = j0 + row;
-            const int64_t off = (((int64_t)b * N + j) * Hkv + g) * D + c * 8;
-            bf16x8 z = {};
-            rk[u] = j < N ? ld16<bf16x8>(k + off) : z;
-            rv[u] = j < N ? ld16<bf16x8>(v + off) : z;
+        for (int u = 0; u < KDMA; ++u) {
+            const int kk = wave * KDMA + u;
+            const int row = kk * (64 / CPR) + lane / CPR;
+            const int gch = (lane % CPR) ^ (row % CPR);
+            const int64_t off = kvbase + (int64_t)min(j0 + row, N - 1) * Hkv * D + gch * 8;
+            dma16(k + off, dst + kk * 1024);
+            dma16(v + off, dst + KBYTES + kk * 1024);
         }
 #pragma unroll
-        for (int u = 0; u < TCH; ++u) {
-            const int e = tid + 256 * u;
-            const int d = e / (KT / 8), c = e % (KT / 8);
-            rt[u] = ld16<bf16x8>(ktb + (int64_t)d * row_len + j0 + c * 8);
+        for (int u = 0; u < TDMA; ++u) {
+            const int kk = wave * TDMA + u;
+            const int d = kk * 8 + lane / 8;
+            const int gsl = (lane % 8) ^ ((d >> 1) & 7);
+            dma16(ktb + (int64_t)d * row_len + j0 + gsl * 8, dst + 2 * KBYTES + kk * 1024);
         }
-        if (tid < KT) rse = (j0 + tid < N) ? seb[j0 + tid] : -1;
-    };
-    auto store_tile = [&](int buf) {
-        char* kb = smem + buf * BUF;
-        char* vb = kb + KBYTES;
-        char* tb = vb + KBYTES;
-#pragma unroll
-        for (int u = 0; u < KCH; ++u) {
-            const int e = tid + 256 * u;
-            const int o = (e / (D / 8)) * KSTR + (e % (D / 8)) * 16;
-            *reinterpret_cast<bf16x8*>(kb + o) = rk[u];
-            *reinterpret_cast<bf16x8*>(vb + o) = rv[u];
-        }
-#pragma unroll
-        for (int u = 0; u < TCH; ++u) {
-            const int e = tid + 256 * u;
-            *reinterpret_cast<bf16x8*>(tb + (e / (KT / 8)) * TSTR + (e % (KT / 8)) * 16) = rt[u];
-        }
-        if (tid < KT) se_s[buf][tid] = rse;
+        if (lane < 8) dma4(seb + min(j0 + wave * 8 + lane, N - 1), dst + 2 * KBYTES + TBYTES + wave * 32);
     };
 
-    int t = next_visible(tmaxb, 0, t_last, i0);
-    int cur = 0;
-    if (t >= 0) {
-        load_tile(t);
-        store_tile(0);
-    }
-    __syncthreads();
-    while (t >= 0) {
-        const int tn = next_visible(tmaxb, t + 1, t_last, i0);
-        if (tn >= 0) load_tile(tn);
-        const int j0 = t * KT;
-        const bool full = (j0 + KT - 1 <= i0) && (tminb[t] >= i_last);
-        const char* kb = smem + cur * BUF;
-        const char* vb = kb + KBYTES;
-        const char* tb = vb + KBYTES;
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            f32x16 st[2], dpt[2];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                zero(st[qb]);
-                zero(dpt[qb]);
-            }
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const int o = (x * 32 + l32) * KSTR + (hi * 8 + 16 * c) * 2;
-                const bf16x8 ak = ld16<bf16x8>(kb + o), av = ld16<bf16x8>(vb + o);
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    st[qb] = mfma32(ak, qf[qb][c], st[qb]);
-                    dpt[qb] = mfma32(av, df[qb][c], dpt[qb]);
+    int resume = 0;
+    while (resume >= 0) {
+        if (wave == 0) {
+            int cnt = 0, next = -1;
+            for (int base = resume; base <= t_last; base += 64) {
+                const int t = base + lane;
+                const bool vis = t <= t_last && tmaxb[t] >= i0;
+                const bool full = vis && (t * KT + KT - 1 <= i0) && tminb[t] >= i_last;
+                const unsigned long long m = __ballot(vis);
+                const int n_m = __popcll(m);
+                if (cnt + n_m > LCAP) {
+                    next = base;
+                    break;
                 }
+                const int pos = cnt + __popcll(m & ((1ull << lane) - 1ull));
+                if (vis) list[pos] = t | (full ? FULL : 0);
+                cnt += n_m;
             }
-            bf16x8 dsf[2][2];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int ip = posb[qb] + l32;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int jj = x * 32 + acc_row(r, hi);
-                    float p = __builtin_amdgcn_exp2f(fmaf(st[qb][r], scale_log2, -l2q[qb]));
-                    if (!full && !(j0 + jj <= ip && ip <= se_s[cur][jj])) p = 0.f;
-                    dsf[qb][r >> 3][r & 7] = (__bf16)(p * (dpt[qb][r] - dlq[qb]));
-                }
+            if (lane == 0) {
+                list_meta[0] = cnt;
+                list_meta[1] = next;
             }
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    const bf16x8 a = ld16<bf16x8>(tb + (db * 32 + l32) * TSTR + (x * 32 + c2 * 16 + hi * 8) * 2);
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) acc[qb][db] = mfma32(a, dsf[qb][c2], acc[qb][db]);
-                }
         }
-        if (tn >= 0) store_tile(cur ^ 1);
         __syncthreads();
-        cur ^= 1;
-        t = tn;
-    }
+        const int cnt = list_meta[0];
+        resume = list_meta[1];
+
+        if (cnt > 0) issue(list[0] & (FULL - 1), 0);
+        if (cnt > 1) issue(list[1] & (FULL - 1), 1);
+        for (int it = 0; it < cnt; ++it) {
+            if (it + 1 < cnt) wait_vmcnt<PER_TILE>();
+            else wait_vmcnt<0>();
+            barrier();
+            if (it + 2 < cnt) issue(list[it + 2] & (FULL - 1), (it + 2) % NSTAGE);
+            const int e = list[it];
+            const int t = e & (FULL - 1);
+            const bool full = (e & FULL) != 0;
+            const int j0 = t * KT;
+            const char* st = smem + (it % NSTAGE) * STAGE;
+            const char* tb = st + 2 * KBYTES;
+            const int* ses = reinterpret_cast<const int*>(tb + TBYTES);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int p = posb[qb] + l32;
-        if (p < N) {
-            __bf16* o = dq + (((int64_t)b * N + p) * Hq + head[qb]) * D;
+            for (int x = 0; x < 2; ++x) {
+                f32x16 sacc, dpt;
+                zero(sacc);
+                zero(dpt);
+                const int row = x * 32 + l32;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int grp = 0; grp < 4; ++grp) {
-                    bf16x4 v4;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[qb][db][grp * 4 + e] * scale);
-                    *reinterpret_cast<bf16x4*>(o + db * 32 + grp * 8 + hi * 4) = v4;
+                for (int c = 0; c < NC; ++c) {
+                    const int o = row * KROW + (((hi + 2 * c) ^ (row % CPR)) * 16);
+                    sacc = mfma32(ld16<bf16x8>(st + o), qf[c], sacc);
+                    dpt = mfma32(ld16<bf16x8>(st + KBYTES + o), df[c], dpt);
                 }
+                bf16x8 dsf[2];
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int jj = x * 32 + 8 * gq + 4 * hi;
+                    int sv[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+                    if (!full) {
+                        const int4 s4 = *reinterpret_cast<const int4*>(ses + jj);
+                        sv[0] = s4.x;
+                        sv[1] = s4.y;
+                        sv[2] = s4.z;
+                        sv[3] = s4.w;
+                    }
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) {
+                        const int r = gq * 4 + e4;
+                        float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -l2q));
+                        if (!full && !(j0 + jj + e4 <= ip && ip <= sv[e4])) p = 0.f;
+                        dsf[r >> 3][r & 7] = (__bf16)(p * (dpt[r] - dlq));
+                    }
+                }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int c2 = 0; c2 < 2; ++c2) {
+                        const int d = db * 32 + l32;
+                        const bf16x8 a = ld16<bf16x8>(tb + d * TROW + (((x * 4 + c2 * 2 + hi) ^ ((d >> 1) & 7)) * 16));
+                        acc[db] = mfma32(a, dsf[c2], acc[db]);
+                    }
+            }
         }
+        __syncthreads();
+    }
+    if (ip < N) {
+        __bf16* o = dq + (((int64_t)b * N + ip) * Hq + head) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                bf16x4 v4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[db][grp * 4 + e] * scale);
+                *reinterpret_cast<bf16x4*>(o + db * 32 + grp * 8 + hi * 4) = v4;
+            }
     }
 }
 
@@ -502,7 +702,7 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
     const int n_chunks = G / HB;
     const int n_qtiles = (a.N + BM - 1) / BM;
     const int64_t blocks = (int64_t)n_qtiles * a.B * a.Hkv * n_chunks;
-    hipLaunchKernelGGL((bwd_dq<D, HB>), dim3((unsigned)blocks), dim3(256), 0, st, (const __bf16*)a.q,
+    hipLaunchKernelGGL((bwd_dq<D, HB>), dim3((unsigned)blocks), dim3(512), 0, st, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, w.delta,
                        (const __bf16*)w.kt, a.se, w.tile_min, w.tile_max, a.B, a.N, a.Hq, a.Hkv, T, n_qtiles,
                        n_chunks, a.scale * kLog2e, a.scale, (__bf16*)a.dq);
@@ -517,11 +717,18 @@ hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) 
                        (__bf16*)w.qt, (__bf16*)w.dot, (__bf16*)w.kt, w.tile_min, w.tile_max);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int n_ktiles = (a.N + 127) / 128;
-    hipLaunchKernelGGL((bwd_dkdv<D>), dim3((unsigned)((int64_t)n_ktiles * a.B * a.Hkv)), dim3(256), 0, st,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                       w.delta, (const __bf16*)w.qt, (const __bf16*)w.dot, a.se, a.B, a.N, a.Hq, a.Hkv, T,
-                       a.scale * kLog2e, a.scale, (__bf16*)a.dk, (__bf16*)a.dv);
+    hipLaunchKernelGGL(bwd_plan, dim3(1), dim3(1024), 0, st, w.tile_max, a.B, a.N, T, a.Hq / a.Hkv, a.Hkv, w.ctrl,
+                       w.tile_plan, w.units, w.split_tiles);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv<D>), dim3((unsigned)num_cus()), dim3(512), 0, st, (const __bf16*)a.q,
+                       (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, w.delta,
+                       (const __bf16*)w.qt, (const __bf16*)w.dot, a.se, a.B, a.N, a.Hq, a.Hkv, T, a.scale * kLog2e,
+                       a.scale, w.ctrl, w.units, w.partial, (__bf16*)a.dk, (__bf16*)a.dv);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_reduce<D>), dim3(kSplitSlots / 2, 8), dim3(256), 0, st, w.ctrl, w.split_tiles, w.partial,
+                       a.N, a.Hkv, (__bf16*)a.dk, (__bf16*)a.dv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     switch (heads_per_wg(a.Hq / a.Hkv)) {
@@ -534,13 +741,22 @@ hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) 
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+size_t plan_bytes(int B, int N, int Hkv, int D) {
+    const size_t T256 = (size_t)(N + 255) / 256;
+    const size_t ucap = (size_t)kSplitSlots + (size_t)B * T256 * Hkv;
+    return align256(32 * sizeof(int)) + align256((size_t)B * T256 * sizeof(int4)) +
+           align256(ucap * 2 * sizeof(int4)) + align256((size_t)(kSplitSlots / 2) * sizeof(int4)) +
+           align256((size_t)kSplitSlots * 2 * 256 * D * sizeof(float));
+}
+
 }  // namespace
 
 size_t mfma_bwd_ws_bytes(int B, int N, int Hq, int Hkv, int D) {
     const size_t T = (size_t)(N + KT - 1) / KT;
     const size_t Np = T * KT;
     return align256((size_t)B * Hq * N * sizeof(float)) + 2 * align256((size_t)B * Hq * D * Np * 2) +
-           align256((size_t)B * Hkv * D * Np * 2) + 2 * align256((size_t)B * T * sizeof(int32_t));
+           align256((size_t)B * Hkv * D * Np * 2) + 2 * align256((size_t)B * T * sizeof(int32_t)) +
+           plan_bytes(B, N, Hkv, D);
 }
 
 BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D) {
@@ -559,6 +775,18 @@ BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D) {
     w.tile_min = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)B * T * sizeof(int32_t));
     w.tile_max = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)B * T * sizeof(int32_t));
+    const size_t T256 = (size_t)(N + 255) / 256;
+    const size_t ucap = (size_t)kSplitSlots + (size_t)B * T256 * Hkv;
+    w.ctrl = reinterpret_cast<int32_t*>(p);
+    p += align256(32 * sizeof(int));
+    w.tile_plan = reinterpret_cast<int4*>(p);
+    p += align256((size_t)B * T256 * sizeof(int4));
+    w.units = reinterpret_cast<int4*>(p);
+    p += align256(ucap * 2 * sizeof(int4));
+    w.split_tiles = reinterpret_cast<int4*>(p);
+    p += align256((size_t)(kSplitSlots / 2) * sizeof(int4));
+    w.partial = reinterpret_cast<float*>(p);
     return w;
 }
 

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
     constexpr int CPR = D / 8;            // 16-byte chunks per K row
     constexpr int KROW = D * 2;           // LDS bytes per K row (16-byte chunks XOR-swizzled by row)
     constexpr int KBYTES = KT * KROW;
-    constexpr int VROW = KT * 2;          // LDS bytes per V^T row (8 chunks, swizzled by row)
+    constexpr int VROW = KT * 2;          // LDS bytes per V^T row (8 chunks, swizzled by row pair)
     constexpr int VBYTES = D * VROW;
     constexpr int STAGE = KBYTES + VBYTES + KT * 4;
     constexpr int NSTAGE = 3;
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
         for (int u = 0; u < VDMA; ++u) {
             const int kk = wave * VDMA + u;
             const int d = kk * 8 + lane / 8;
-            const int gsl = (lane % 8) ^ (d % 8);
+            const int gsl = (lane % 8) ^ ((d >> 1) & 7);
             dma16(vtb + (int64_t)d * vt_row + j0 + gsl * 8, dst + KBYTES + kk * 1024);
         }
         if (lane < 8) dma4(seb + min(j0 + wave * 8 + lane, N - 1), dst + KBYTES + VBYTES + wave * 32);
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
                     for (int c2 = 0; c2 < 2; ++c2) {
                         const int d = db * 32 + l32;
                         const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                            st + KBYTES + d * VROW + (((x * 4 + c2 * 2 + hi) ^ (d % 8)) * 16));
+                            st + KBYTES + d * VROW + (((x * 4 + c2 * 2 + hi) ^ ((d >> 1) & 7)) * 16));
                         acc[db] = mfma32(a, pf[x][c2], acc[db]);
                     }
         }

@@ -100,6 +100,14 @@ def test_random_tree_bf16_no_rope_and_rope(rope):
     _run_full(w, rope=rope, label=f"random_tree_bf16_rope={rope}")
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(2, 2, 64), (4, 1, 64), (8, 1, 128), (16, 2, 128), (3, 3, 128)])
+def test_random_tree_bf16_head_shapes(Hq, Hkv, D):
+    """Every GQA grouping the matrix-core kernels specialise (1, 4, 8 heads per KV head), head dim 64,
+    and a ratio they do not cover (3 KV heads of 1), which runs on the vector path."""
+    w = _random_workload(700 + Hq * 10 + D, "bf16", Hq=Hq, Hkv=Hkv, D=D, n_seqs=7, max_len=400)
+    _run_full(w, label=f"random_tree_bf16_Hq{Hq}_Hkv{Hkv}_D{D}")
+
+
 def test_degenerate_rows():
     # a single token; a single chain shorter than a tile; a row that is all padding but one slot
     for seqs in ([[5]], [list(range(37))], [[1, 2], [1, 3]]):
