@@ -93,7 +93,7 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
     constexpr int VROW = KT * 2;          // LDS bytes per V^T row (8 chunks, swizzled by row pair)
     constexpr int VBYTES = D * VROW;
     constexpr int STAGE = KBYTES + VBYTES + KT * 4;
-    constexpr int NSTAGE = 3;
+    constexpr int NSTAGE = 4;
     constexpr int KDMA = KBYTES / 1024 / 8;   // 1 KB loads per wave per K tile
     constexpr int VDMA = VBYTES / 1024 / 8;
     constexpr int PER_TILE = KDMA + VDMA + 1; // vector memory ops per wave per tile
@@ -141,25 +141,34 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
     const __bf16* vtb = vt + ((int64_t)b * Hkv + g) * D * vt_row;
     const __bf16* kb_ = k + ((int64_t)b * N * Hkv + g) * D;
 
-    // all of this wave's loads of one tile: K rows (swizzled), V^T rows (swizzled), subtree_end
+    // all of this wave's loads of one tile: K rows (swizzled), V^T rows (swizzled),
+    // subtree_end.  Per-lane source offsets inside a tile are fixed, so they
+    // are computed once; rows past the end of the row are clamped (last tile).
+    int koff[KDMA], krow[KDMA], voff[VDMA];
+#pragma unroll
+    for (int u = 0; u < KDMA; ++u) {
+        const int kk = wave * KDMA + u;
+        krow[u] = kk * (64 / CPR) + lane / CPR;
+        koff[u] = ((lane % CPR) ^ (krow[u] % CPR)) * 8;
+    }
+#pragma unroll
+    for (int u = 0; u < VDMA; ++u) {
+        const int kk = wave * VDMA + u;
+        const int d = kk * 8 + lane / 8;
+        voff[u] = d * (int)vt_row + ((lane % 8) ^ ((d >> 1) & 7)) * 8;
+    }
+    const int64_t kstride = (int64_t)Hkv * D;
     auto issue = [&](int t, int stage) {
         char* dst = smem + stage * STAGE;
         const int j0 = t * KT;
+        const bool tail = j0 + KT > N;
 #pragma unroll
         for (int u = 0; u < KDMA; ++u) {
-            const int kk = wave * KDMA + u;  // which 1 KB of the K tile
-            const int row = kk * (64 / CPR) + lane / CPR;
-            const int gch = (lane % CPR) ^ (row % CPR);
-            const int j = min(j0 + row, N - 1);
-            dma16(kb_ + (int64_t)j * Hkv * D + gch * 8, dst + kk * 1024);
+            const int j = tail ? min(j0 + krow[u], N - 1) : j0 + krow[u];
+            dma16(kb_ + j * kstride + koff[u], dst + (wave * KDMA + u) * 1024);
         }
 #pragma unroll
-        for (int u = 0; u < VDMA; ++u) {
-            const int kk = wave * VDMA + u;
-            const int d = kk * 8 + lane / 8;
-            const int gsl = (lane % 8) ^ ((d >> 1) & 7);
-            dma16(vtb + (int64_t)d * vt_row + j0 + gsl * 8, dst + KBYTES + kk * 1024);
-        }
+        for (int u = 0; u < VDMA; ++u) dma16(vtb + j0 + voff[u], dst + KBYTES + (wave * VDMA + u) * 1024);
         if (lane < 8) dma4(seb + min(j0 + wave * 8 + lane, N - 1), dst + KBYTES + VBYTES + wave * 32);
     };
 
@@ -191,23 +200,20 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
         const int cnt = list_meta[0];
         resume = list_meta[1];
 
-        if (cnt > 0) issue(list[0] & (FULL - 1), 0);
-        if (cnt > 1) issue(list[1] & (FULL - 1), 1);
-        for (int it = 0; it < cnt; ++it) {
-            if (it + 1 < cnt) wait_vmcnt<PER_TILE>();
+        // Software pipeline: S for tile it+1 is issued next to the softmax and
+        // PV product of tile it, so the matrix core has work while the VALU
+        // computes probabilities.  Stage it % 4 holds tile it (its V^T and
+        // subtree_end are still read), stage (it+1) % 4 tile it+1 (its K is
+        // read), and up to two more tiles are in flight.
+        // Wait until this wave's loads of a tile have landed, given how many
+        // tiles were issued after it, then publish every wave's share.
+        auto wait_tile = [&](int ahead) {
+            if (ahead >= 2) wait_vmcnt<2 * PER_TILE>();
+            else if (ahead == 1) wait_vmcnt<PER_TILE>();
             else wait_vmcnt<0>();
             barrier();
-            if (it + 2 < cnt) issue(list[it + 2] & (FULL - 1), (it + 2) % NSTAGE);
-            const int e = list[it];
-            const int t = e & (FULL - 1);
-            const bool full = (e & FULL) != 0;
-            const int j0 = t * KT;
-            const char* st = smem + (it % NSTAGE) * STAGE;
-
-            // S^T = K Q^T: 64 keys x this wave's 32 queries
-            f32x16 sacc[2];
-            zero(sacc[0]);
-            zero(sacc[1]);
+        };
+        auto s_product = [&](const char* st, f32x16 (&sacc)[2]) {  // S^T = K Q^T for one tile
 #pragma unroll
             for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -215,8 +221,29 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
                     const int row = x * 32 + l32;
                     const bf16x8 a = *reinterpret_cast<const bf16x8*>(
                         st + row * KROW + (((hi + 2 * c) ^ (row % CPR)) * 16));
-                    sacc[x] = mfma32(a, qf[c], sacc[x]);
+                    sacc[x] = c == 0 ? mfma32(a, qf[c], f32x16{}) : mfma32(a, qf[c], sacc[x]);
                 }
+        };
+#pragma unroll
+        for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
+            if (s0 < cnt) issue(list[s0] & (FULL - 1), s0);
+        f32x16 scur[2], snext[2];
+        wait_tile(min(NSTAGE - 2, cnt - 1));  // tiles 1 and 2 may still be in flight
+        s_product(smem, snext);
+        for (int it = 0; it < cnt; ++it) {
+            const int e = list[it];
+            const int t = e & (FULL - 1);
+            const bool full = (e & FULL) != 0;
+            const int j0 = t * KT;
+            const char* st = smem + (it % NSTAGE) * STAGE;
+            scur[0] = snext[0];
+            scur[1] = snext[1];
+            const bool more = it + 1 < cnt;
+            if (more) {
+                // issued so far: tiles up to it + 2, so at most one after tile it + 1
+                wait_tile(min(1, cnt - 2 - it));
+                if (it + NSTAGE - 1 < cnt) issue(list[it + NSTAGE - 1] & (FULL - 1), (it + NSTAGE - 1) % NSTAGE);
+            }
             if (!full) {
                 const int* ses = reinterpret_cast<const int*>(st + KBYTES + VBYTES);
 #pragma unroll
@@ -228,7 +255,7 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
                         const int sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
                         for (int e4 = 0; e4 < 4; ++e4)
-                            if (!(j0 + jj + e4 <= ip && ip <= sv[e4])) sacc[x][gq * 4 + e4] = -INFINITY;
+                            if (!(j0 + jj + e4 <= ip && ip <= sv[e4])) scur[x][gq * 4 + e4] = -INFINITY;
                     }
             }
             // online softmax; the running max is only raised (and the output
@@ -237,8 +264,8 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[x][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[x][r]);
+            mx = max_xor32(mx);
             const float mxs = mx * scale_log2;
             if (__ballot(mxs > m_run + 8.f)) {
                 const float m_new = fmaxf(m_run, mxs);
@@ -251,13 +278,17 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
                 m_run = m_new;
             }
             const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            // From here on one straight-line block: the next tile's S product
+            // (on the last tile it re-reads this stage and is discarded), the
+            // probabilities of this tile, and its PV product.
+            s_product(smem + ((more ? it + 1 : it) % NSTAGE) * STAGE, snext);
             bf16x8 pf[2][2];
             float rs = 0.f;
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[x][r], scale_log2, -m_use));
+                    const float p = __builtin_amdgcn_exp2f(fmaf(scur[x][r], scale_log2, -m_use));
                     rs += p;
                     pf[x][r >> 3][r & 7] = (__bf16)p;
                 }
@@ -279,7 +310,7 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
     }
 
     // epilogue: O = O^T / l, lse = (m + log2 l) ln 2
-    const float lt = l_run + __shfl_xor(l_run, 32, 64);
+    const float lt = add_xor32(l_run);
     if (ip < N) {
         const float inv = 1.f / lt;
         __bf16* o = out + (((int64_t)b * N + ip) * Hq + head) * D;

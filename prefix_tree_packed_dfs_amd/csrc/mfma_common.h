@@ -58,14 +58,24 @@ __device__ __forceinline__ int next_visible(const int32_t* __restrict__ tmaxb, i
 // flight across it.  Every wave must wait for its own loads before the
 // barrier that publishes them.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glob_void_t;
-
+// The loads are written as inline assembly: through the compiler builtin,
+// the wait-count pass cannot tell the DMA's LDS destination from the stage
+// being read and drains every in-flight prefetch (vmcnt(0)) before each LDS
+// read.  As assembly they are invisible to that pass; the explicit waits
+// below carry the dependency.  Vector memory operations complete in issue
+// order, so the compiler's own waits for older loads stay correct.
+// LDS byte address of a pointer into shared memory, as a wave-uniform scalar
+// (callers pass per-wave bases; readfirstlane puts them in an SGPR for M0).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
-    __builtin_amdgcn_global_load_lds((glob_void_t*)gsrc, (lds_void_t*)lds_base, 16, 0, 0);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds_addr(lds_base))
+                 : "memory");
 }
 __device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
-    __builtin_amdgcn_global_load_lds((glob_void_t*)gsrc, (lds_void_t*)lds_base, 4, 0, 0);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "s"(lds_addr(lds_base))
+                 : "memory");
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -77,5 +87,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// max / sum of a value with the lane 32 positions away (v_permlane32_swap
+// exchanges the two halves of a wave without going through LDS).
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 }  // namespace treeattn
