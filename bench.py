@@ -31,6 +31,37 @@ WORKLOADS = {
     "long_history": 5,
 }
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+COPY_BYTES = 1 << 30         # size of the plain copy used to calibrate the HBM byte counters
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources: counter-based traffic is only reported for the kernels it was taken on."""
+    import hashlib
+    d = os.path.join(ROOT, "prefix_tree_packed_dfs_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".cpp", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per backward call from profiles/<workload>_traffic.md, if taken on these sources."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(vals["bwd_traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
 
 
 def describe(w, n, R, pairs):
@@ -96,6 +127,8 @@ def main():
     ap.add_argument("--workload", default="grpo_group", choices=list(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 1 GiB (for calibrating HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -112,6 +145,14 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}), flush=True)
+        return
     w = standard(WORKLOADS[args.workload])
     if not w.backward:
         w.backward = True  # time the full path on every workload
@@ -235,8 +276,9 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
         },
+        "source_hash": source_hash(),
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, total_flops, args.cpu_seconds)
