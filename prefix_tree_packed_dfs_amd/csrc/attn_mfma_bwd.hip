@@ -143,104 +143,171 @@ __global__ __launch_bounds__(256) void bwd_prep(const __bf16* __restrict__ q, co
 
 // ---------------------------------------------------------------------------
 // dK/dV work plan (one workgroup).  A KV tile of 256 keys visits every
-// (32-position block, query head) pair from its first key to the largest
-// subtree_end among its keys.  Keys of a long shared prefix visit almost the
-// whole row while keys near the leaves visit a few blocks, so tiles whose
-// visit count exceeds the budget are split into chunks; the budget doubles
-// until the chunks fit the partial-sum slots.  Units are queued per KV head
-// group (g mod NQ, so one XCD keeps one head's data in its L2), split chunks
-// first, then whole tiles.
+// (32-position block, query head) pair from its first key's block to the
+// block of the largest subtree_end among its keys.  Keys of a long shared
+// prefix visit almost the whole row while keys near the leaves visit a few
+// blocks, so a tile whose range exceeds C blocks is cut at multiples of C
+// (absolute block positions, C = budget / G; the budget doubles until the
+// chunks fit the partial-sum slots).  Units are then queued bucket by bucket
+// of C query blocks: the units that run together on one XCD read the same
+// query blocks, which stay in its L2.  Each KV head has its own queue
+// (g mod NQ, so one XCD keeps one head's data).  The order of units inside
+// a bucket is arbitrary; every unit's result is the same whatever the order.
 // ctrl: [0..7] queue counters, [8..15] lengths, [16..23] starts, [24] split tiles.
+// tile_plan[u]: {first block, last block, chunks, first slot or -1}.
 // ---------------------------------------------------------------------------
+constexpr int kPlanBuckets = 4096;
+
+__device__ int block_exclusive_scan(int v, int* s_scan) {
+    const int tid = threadIdx.x;
+    s_scan[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int x = tid >= off ? s_scan[tid - off] : 0;
+        __syncthreads();
+        s_scan[tid] += x;
+        __syncthreads();
+    }
+    const int r = s_scan[tid] - v;
+    __syncthreads();
+    return r;
+}
+
 __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tmax, int B, int N, int T, int G,
                                                  int Hkv, int* __restrict__ ctrl, int4* __restrict__ tile_plan,
                                                  int4* __restrict__ units, int4* __restrict__ split_tiles) {
-    __shared__ int s_sum, s_budget, s_tot[3];
+    __shared__ int s_sum, s_budget;
+    __shared__ int s_scan[1024];
+    __shared__ int s_cnt[kPlanBuckets];
     const int tid = threadIdx.x;
     const int T256 = (N + 255) / 256;
     const int BT = B * T256;
+    const int NB = (N + 31) / 32;
     const int NQ = Hkv < 8 ? Hkv : 8;
     for (int u = tid; u < BT; u += 1024) {
         const int b = u / T256, t = u % T256;
         int qmax = -1;
         for (int x = 4 * t; x < min(4 * t + 4, T); ++x) qmax = max(qmax, tmax[(int64_t)b * T + x]);
-        const int nv = (qmax / 32 - (t * 256) / 32 + 1) * G;
-        tile_plan[u] = make_int4(nv, 1, 0, 0);
+        tile_plan[u] = make_int4(8 * t, max(qmax / 32, 8 * t), 1, -1);
     }
     if (tid == 0) s_budget = kVisitBudget;
     __syncthreads();
+    int C;
     for (;;) {
         if (tid == 0) s_sum = 0;
         __syncthreads();
-        const int budget = s_budget;
+        C = max(1, s_budget / G);
         int part = 0;
         for (int u = tid; u < BT; u += 1024) {
-            const int nv = tile_plan[u].x;
-            if (nv > budget) part += (nv + budget - 1) / budget;
+            const int4 e = tile_plan[u];
+            if (e.y - e.x + 1 > C) part += e.y / C - e.x / C + 1;
         }
         if (part) atomicAdd(&s_sum, part);
         __syncthreads();
         const bool fits = (int64_t)s_sum * Hkv <= kSplitSlots;
         __syncthreads();
         if (fits) break;
-        if (tid == 0) s_budget = budget * 2;
+        if (tid == 0) s_budget *= 2;
         __syncthreads();
     }
-    const int budget = s_budget;
-    if (tid == 0) {  // compaction (sequential: one entry per 256-key tile of the batch)
-        int n_split = 0, n_single = 0, slot = 0;
-        for (int u = 0; u < BT; ++u) {
+    // chunks per tile; slots and split-tile indices by an exclusive scan in tile order
+    const int per = (BT + 1023) / 1024;
+    const int u0 = min(BT, tid * per), u1 = min(BT, u0 + per);
+    int my_chunks = 0, my_split = 0, my_units = 0;
+    for (int u = u0; u < u1; ++u) {
+        const int4 e = tile_plan[u];
+        const int nc = e.y - e.x + 1 > C ? e.y / C - e.x / C + 1 : 1;
+        if (nc > 1) {
+            my_chunks += nc;
+            my_split += 1;
+        }
+        my_units += nc;
+    }
+    // chunk and split counts are at most kSplitSlots: pack both in one scan
+    const int packed = block_exclusive_scan(my_chunks | (my_split << 16), s_scan);
+    const int n_units = [&] {
+        const int before = block_exclusive_scan(my_units, s_scan);
+        if (tid == 1023) s_sum = before + my_units;
+        __syncthreads();
+        return s_sum;
+    }();
+    {
+        int slot = packed & 0xFFFF, z = packed >> 16;
+        for (int u = u0; u < u1; ++u) {
             int4 e = tile_plan[u];
-            if (e.x > budget) {
-                e.y = (e.x + budget - 1) / budget;
-                e.z = n_split++;
+            const int nc = e.y - e.x + 1 > C ? e.y / C - e.x / C + 1 : 1;
+            if (nc > 1) {
+                e.z = nc;
                 e.w = slot;
-                slot += e.y;
-                split_tiles[e.z] = make_int4(u / T256, u % T256, e.w, e.y);
-            } else {
-                e.y = 1;
-                e.z = n_single++;
-                e.w = -1;
+                split_tiles[z] = make_int4(u / T256, u % T256, slot, nc);
+                slot += nc;
+                ++z;
             }
             tile_plan[u] = e;
         }
-        s_tot[0] = slot;       // chunks of split tiles (per head)
-        s_tot[1] = n_single;
-        s_tot[2] = n_split;
-        int start = 0;
-        for (int x = 0; x < NQ; ++x) {
-            const int hg = (Hkv - x + NQ - 1) / NQ;  // heads in queue x
-            ctrl[x] = 0;
-            ctrl[8 + x] = (slot + n_single) * hg;
-            ctrl[16 + x] = start;
-            start += (slot + n_single) * hg;
+        if (tid == 1023) {
+            ctrl[24] = z;
+            int start = 0;
+            for (int x = 0; x < NQ; ++x) {
+                const int hg = (Hkv - x + NQ - 1) / NQ;  // heads in queue x
+                ctrl[x] = 0;
+                ctrl[8 + x] = n_units * hg;
+                ctrl[16 + x] = start;
+                start += n_units * hg;
+            }
         }
-        ctrl[24] = n_split;
+    }
+    // bucket of a unit: (row, C-block range of its first block), coarsened to fit kPlanBuckets
+    const int NBK = (NB + C - 1) / C;
+    int shift = 0;
+    while ((((int64_t)B * NBK - 1) >> shift) >= kPlanBuckets) ++shift;
+    for (int x = tid; x < kPlanBuckets; x += 1024) s_cnt[x] = 0;
+    __syncthreads();
+    for (int u = u0; u < u1; ++u) {
+        const int4 e = tile_plan[u];
+        const int kb = (u / T256) * NBK + e.x / C;
+        for (int kk = 0; kk < e.z; ++kk) atomicAdd(&s_cnt[(kb + kk) >> shift], 1);
     }
     __syncthreads();
-    const int chunks = s_tot[0];
-    for (int u = tid; u < BT; u += 1024) {
+    {  // exclusive scan of the bucket counts, four per thread
+        int c4[4], s = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c4[i] = s_cnt[4 * tid + i];
+            s += c4[i];
+        }
+        int off = block_exclusive_scan(s, s_scan);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s_cnt[4 * tid + i] = off;
+            off += c4[i];
+        }
+    }
+    __syncthreads();
+    for (int u = u0; u < u1; ++u) {
         const int4 e = tile_plan[u];
         const int b = u / T256, t = u % T256;
-        for (int g = 0; g < Hkv; ++g) {
-            const int x = g % NQ, r = g / NQ, hg = (Hkv - x + NQ - 1) / NQ;
-            const int qs = ctrl[16 + x];
-            if (e.w >= 0) {
-                const int per = (e.x + e.y - 1) / e.y;
-                for (int kk = 0; kk < e.y; ++kk) {
-                    const int idx = qs + (e.w + kk) * hg + r;
-                    units[2 * idx] = make_int4(b * Hkv + g, t, kk * per, min((kk + 1) * per, e.x));
-                    units[2 * idx + 1] = make_int4((e.w + kk) * Hkv + g, 0, 0, 0);
-                }
-            } else {
-                const int idx = qs + (chunks + e.z) * hg + r;
-                units[2 * idx] = make_int4(b * Hkv + g, t, 0, e.x);
-                units[2 * idx + 1] = make_int4(-1, 0, 0, 0);
+        const int kb = b * NBK + e.x / C;
+        for (int kk = 0; kk < e.z; ++kk) {
+            const int pos = atomicAdd(&s_cnt[(kb + kk) >> shift], 1);
+            int v0 = 0, v1 = (e.y - e.x + 1) * G, slot = -1;
+            if (e.z > 1) {
+                const int k = e.x / C + kk;
+                v0 = (max(e.x, k * C) - e.x) * G;
+                v1 = (min(e.y, k * C + C - 1) - e.x + 1) * G;
+                slot = e.w + kk;
+            }
+            for (int g = 0; g < Hkv; ++g) {
+                const int x = g % NQ, r = g / NQ, hg = (Hkv - x + NQ - 1) / NQ;
+                const int idx = ctrl[16 + x] + pos * hg + r;
+                units[2 * idx] = make_int4(b * Hkv + g, t, v0, v1);
+                units[2 * idx + 1] = make_int4(slot >= 0 ? slot * Hkv + g : -1, 0, 0, 0);
             }
         }
     }
 }
 
+// ---------------------------------------------------------------------------
 // Sum the chunk partials of split tiles in chunk order and write bf16 dK, dV.
 // grid (kSplitSlots / 2 [an upper bound on split tiles x KV heads], 8 chunks
 // of 32 keys), 256 threads.

@@ -33,6 +33,34 @@ __device__ __forceinline__ void zero(f32x16& x) {
     for (int r = 0; r < 16; ++r) x[r] = 0.f;
 }
 
+// Position of 16-byte chunk c of a row of D bf16 values in LDS: c ^ row_swizzle<D>(row).
+// Two read patterns touch these rows.  Operand loads (ds_read_b128) take one
+// chunk of 16 consecutive rows per 16 lanes; transposed loads
+// (ds_read_b64_tr_b16) take 4 consecutive rows x 4 consecutive chunks per
+// half wave.  With 64 four-byte banks both hit 16 distinct 16-byte bank
+// groups: the swizzle is a bijection on row % 16, and the four rows of an
+// aligned quad land in four different chunk quads (D = 128: rows of 256
+// bytes) or in two chunk quads of the two row parities (D = 64: rows of 128
+// bytes, two rows per 256-byte bank window).
+template <int D>
+__device__ __forceinline__ int row_swizzle(int r) {
+    static_assert(D == 64 || D == 128, "head dim");
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Transposed LDS load (checked on gfx950 with an in-bounds probe): in each
+// group of 16 lanes, lane i receives element i % 4 of the 8 bytes addressed
+// by lanes 4k + i / 4 of the group, k = 0..3, in that order.  Two such loads
+// give the 8 values of one MFMA operand: lo fills slots 0-3, hi slots 4-7.
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+__device__ __forceinline__ bf16x8 ld_tr(const void* lo, const void* hi) {
+    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+    const bf16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(lo));
+    const bf16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(hi));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // First tile index >= from (and <= t_last) whose largest subtree_end reaches
 // i0; -1 if none.  Wave-uniform: 64 tiles are tested per step with one ballot.
 __device__ __forceinline__ int next_visible(const int32_t* __restrict__ tmaxb, int from, int t_last, int i0) {
