@@ -27,9 +27,8 @@ struct FwdWorkspace {
 // Workspace carved by the backward.
 struct BwdWorkspace {
     float* delta;        // [B, Hq, N]  rowsum(dout * out)
-    uint16_t* qt;        // bf16 bits [B, Hq, D, T*KT]  Q^T, rows permuted in 16-row groups
-    uint16_t* dot;       // bf16 bits [B, Hq, D, T*KT]  dout^T, same layout
-    uint16_t* kt;        // bf16 bits [B, Hkv, D, T*KT] K^T, same layout
+    float* lse2;         // [B, Hq, N]  lse * log2(e)
+    uint16_t* kt;        // bf16 bits [B, Hkv, D, T*KT] K^T, rows permuted in 16-row groups
     int32_t* tile_min;   // [B, T]
     int32_t* tile_max;   // [B, T]
     // dK/dV work plan: KV tiles of 256 keys whose query range is long are split

@@ -23,6 +23,7 @@
 // dK/dV and dQ recompute S and dP separately (7 products instead of 5) so
 // that no partial dQ has to be summed across workgroups.
 #include <climits>
+#include <type_traits>
 
 #include "attn_mfma.h"
 #include "mfma_common.h"
@@ -51,31 +52,21 @@ int num_cus() {
     return cached[dev];
 }
 
-// grid (T, Hq, B), 256 threads
+// grid (T, Hq, B), 256 threads: delta and lse * log2(e) per (row, query
+// head), K^T per KV head (rows permuted in 16-row groups), and the per-tile
+// subtree_end range.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_prep(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                                                const __bf16* __restrict__ out, const __bf16* __restrict__ dout,
+__global__ __launch_bounds__(256) void bwd_prep(const __bf16* __restrict__ k, const __bf16* __restrict__ out,
+                                                const __bf16* __restrict__ dout, const float* __restrict__ lse,
                                                 const int32_t* __restrict__ se, int N, int Hq, int Hkv, int T,
-                                                float* __restrict__ delta, __bf16* __restrict__ qt,
-                                                __bf16* __restrict__ dot, __bf16* __restrict__ ktr,
-                                                int32_t* __restrict__ tmin, int32_t* __restrict__ tmax) {
+                                                float* __restrict__ delta, float* __restrict__ lse2,
+                                                __bf16* __restrict__ ktr, int32_t* __restrict__ tmin,
+                                                int32_t* __restrict__ tmax) {
     constexpr int CPR = D / 8;
     __shared__ __attribute__((aligned(16))) __bf16 ta[KT][D + 8];
-    __shared__ __attribute__((aligned(16))) __bf16 tb[KT][D + 8];
     const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int j0 = t * KT;
     const int64_t row_len = (int64_t)T * KT;
-    for (int e = tid; e < KT * CPR; e += 256) {
-        const int r = e / CPR, c = e % CPR, j = j0 + r;
-        bf16x8 vq = {}, vd = {};
-        if (j < N) {
-            const int64_t off = (((int64_t)b * N + j) * Hq + h) * D + c * 8;
-            vq = ld16<bf16x8>(q + off);
-            vd = ld16<bf16x8>(dout + off);
-        }
-        *reinterpret_cast<bf16x8*>(&ta[r][c * 8]) = vq;
-        *reinterpret_cast<bf16x8*>(&tb[r][c * 8]) = vd;
-    }
     {  // delta: four threads per row
         const int r = tid >> 2, part = tid & 3, j = j0 + r;
         float s = 0.f;
@@ -90,26 +81,13 @@ __global__ __launch_bounds__(256) void bwd_prep(const __bf16* __restrict__ q, co
         }
         s += __shfl_xor(s, 1, 64);
         s += __shfl_xor(s, 2, 64);
-        if (part == 0 && j < N) delta[((int64_t)b * Hq + h) * N + j] = s;
-    }
-    __syncthreads();
-    __bf16* dst_q = qt + ((int64_t)b * Hq + h) * D * row_len + j0;
-    __bf16* dst_d = dot + ((int64_t)b * Hq + h) * D * row_len + j0;
-    for (int e = tid; e < D * (KT / 8); e += 256) {
-        const int d = e / (KT / 8), c = e % (KT / 8);
-        bf16x8 oq, od;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int p = c * 8 + u;
-            const int row = (p >> 4) * 16 + inv_phys16(p & 15);
-            oq[u] = ta[row][d];
-            od[u] = tb[row][d];
+        if (part == 0 && j < N) {
+            const int64_t ro = ((int64_t)b * Hq + h) * N + j;
+            delta[ro] = s;
+            lse2[ro] = lse[ro] * kLog2e;
         }
-        *reinterpret_cast<bf16x8*>(dst_q + (int64_t)d * row_len + c * 8) = oq;
-        *reinterpret_cast<bf16x8*>(dst_d + (int64_t)d * row_len + c * 8) = od;
     }
     if (h < Hkv) {  // K^T of KV head h
-        __syncthreads();
         for (int e = tid; e < KT * CPR; e += 256) {
             const int r = e / CPR, c = e % CPR, j = j0 + r;
             bf16x8 vk = {};
@@ -351,44 +329,61 @@ __global__ __launch_bounds__(256) void bwd_reduce(const int* __restrict__ ctrl,
 
 // ---------------------------------------------------------------------------
 // dK, dV: persistent, one 512-thread workgroup per CU (8 waves x 32 keys);
-// work units come from the plan's queues
+// work units come from the plan's queues.  A visit is 32 positions of one
+// query head: its stage holds those Q and dout rows as they are in memory
+// (16-byte chunks swizzled), lse * log2(e) and delta.  S = Q K^T and
+// dP = dout V^T read Q and dout rows as the A operand; dV^T += dout^T P and
+// dK^T += Q^T dS read the same rows through transposed LDS loads.  K sits in
+// registers, V in this wave's own LDS rows.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                    const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
-                                                   const float* __restrict__ lse, const float* __restrict__ delta,
-                                                   const __bf16* __restrict__ qt, const __bf16* __restrict__ dot,
-                                                   const int32_t* __restrict__ se, int B, int N, int Hq, int Hkv,
-                                                   int T, float scale_log2, float scale, int* __restrict__ ctrl,
+                                                   const float* __restrict__ lse2, const float* __restrict__ delta,
+                                                   const int32_t* __restrict__ se, int N, int Hq, int Hkv,
+                                                   float scale_log2, float scale, int* __restrict__ ctrl,
                                                    const int4* __restrict__ units, float* __restrict__ partial,
                                                    __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
     constexpr int NC = D / 16, NDB = D / 32;
-    constexpr int CPR = D / 8;             // 16-byte chunks per natural row
-    constexpr int NROW = D * 2;            // LDS bytes per natural row (32 rows per visit)
-    constexpr int NBYTES = 32 * NROW;
-    constexpr int TROW = 64;               // LDS bytes per transposed row (32 positions)
-    constexpr int TBYTES = D * TROW;
-    constexpr int STAGE = 2 * NBYTES + 2 * TBYTES + 256;
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int NROW = D * 2;            // bytes per row
+    constexpr int NBYTES = 32 * NROW;      // 32 rows
+    constexpr int STAGE = 2 * NBYTES + 256;
     constexpr int NSTAGE = 4;
-    // 16-byte chunks each wave loads per tile; below 64 a single load with
-    // only the first lanes active (head dim 64)
+    // 16-byte chunks each wave loads per array and visit; below 64 a single
+    // load with only the first lanes active (head dim 64)
     constexpr int NCH = NBYTES / 16 / 8;
-    constexpr int TCH = TBYTES / 16 / 8;
     constexpr int NDMA = NCH >= 64 ? NCH / 64 : 1;
-    constexpr int TDMA = TCH >= 64 ? TCH / 64 : 1;
     constexpr int NLANES = NCH >= 64 ? 64 : NCH;
-    constexpr int TLANES = TCH >= 64 ? 64 : TCH;
-    constexpr int PER_VISIT = 2 * NDMA + 2 * TDMA + 1;
+    constexpr int PER_VISIT = 2 * NDMA + 1;
+    constexpr int VDMA = NBYTES / 1024;    // this wave's 32 V rows
     static_assert(NSTAGE == 4 && 2 * PER_VISIT < 16, "wait counts below assume four stages");
     __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
-    __shared__ int qmax_s[8];
+    __shared__ __attribute__((aligned(1024))) char vrows[8 * NBYTES];
     __shared__ int4 unit_s[2];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: bases stay scalar
     const int l32 = lane & 31, hi = lane >> 5;
     const int G = Hq / Hkv;
     const int NQ = Hkv < 8 ? Hkv : 8;
     const int qx = blockIdx.x % NQ;
+    char* const vw = vrows + wave * NBYTES;
+    // operand loads: row l32, chunk 2c + hi = 2c ^ hi, stored at 2c ^ (hi ^ swizzle)
+    const int nat = l32 * NROW;
+    const int nat_x = (hi ^ row_swizzle<D>(l32)) * 16;
+    // transposed loads: this lane supplies row 4 (lane / 32) + (lane / 4) % 4 (+ 8 for
+    // slots 4-7, + 16 per 16-row chunk) and column 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4)
+    int tr_off[NDB][2];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int row = 4 * (lane >> 5) + ((lane >> 2) & 3) + 8 * half;
+            const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+            tr_off[db][half] = row * NROW + ((chunk ^ row_swizzle<D>(row)) * 16) + 8 * (lane & 1);
+        }
+
     for (;;) {
     if (tid == 0) {
         const int idx = atomicAdd(&ctrl[qx], 1);
@@ -400,12 +395,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
         }
     }
     __syncthreads();
-    const int4 un = unit_s[0];
-    const int slot = unit_s[1].x;
-    if (un.x < 0) break;
-    const int g = un.x % Hkv, b = un.x / Hkv;
-    const int j0 = un.y * 256;
-    const int v_begin = un.z;
+    // unit fields are wave-uniform: keep them (and all address bases) in SGPRs
+    const int ux = __builtin_amdgcn_readfirstlane(unit_s[0].x);
+    const int slot = __builtin_amdgcn_readfirstlane(unit_s[1].x);
+    if (ux < 0) break;
+    const int g = ux % Hkv, b = ux / Hkv;
+    const int j0 = __builtin_amdgcn_readfirstlane(unit_s[0].y) * 256;
+    const int v_begin = __builtin_amdgcn_readfirstlane(unit_s[0].z);
+    const int v_end = __builtin_amdgcn_readfirstlane(unit_s[0].w);
     const int j0w = j0 + 32 * wave;
     const int jk = j0w + l32;
     const bool kvalid = jk < N;
@@ -414,31 +411,49 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
     const int wmax = wave_max_i32(sek);
     const int wmin = wave_min_i32(kvalid ? sek : INT_MAX);
 
-    bf16x8 kf[NC], vf[NC];
+    // this wave's V rows into LDS (swizzled like the stage rows)
+    {
+        const int r0 = min(j0w, N - 1);  // a wave past the end still loads rows in bounds
+        const __bf16* vb = v + (((int64_t)b * N + r0) * Hkv + g) * D;
+        const int lim = N - 1 - r0;
+#pragma unroll
+        for (int u = 0; u < VDMA; ++u) {
+            const int e = u * 64 + lane;
+            const int row = e / CPR;
+            const int gch = (e % CPR) ^ row_swizzle<D>(row);
+            dma16s(vb, (uint32_t)(min(row, lim) * Hkv * D + gch * 8) * 2u, vw + u * 1024);
+        }
+    }
+    bf16x8 kf[NC];
     {
         const int64_t off = (((int64_t)b * N + min(jk, N - 1)) * Hkv + g) * D + hi * 8;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             bf16x8 z = {};
             kf[c] = kvalid ? ld16<bf16x8>(k + off + 16 * c) : z;
-            vf[c] = kvalid ? ld16<bf16x8>(v + off + 16 * c) : z;
         }
     }
+    // K (and the V rows) complete before any prefetch is issued: the
+    // compiler's own wait for K then sits here, not inside the visit loop
+    // where it would drain every prefetch
+    wait_vmcnt<0>();
     f32x16 dkt[NDB], dvt[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
         zero(dkt[db]);
         zero(dvt[db]);
     }
-    if (lane == 0) qmax_s[wave] = wmax;
-    __syncthreads();
-    int qmax = qmax_s[0];
-#pragma unroll
-    for (int w = 1; w < 8; ++w) qmax = max(qmax, qmax_s[w]);
     const int pb0 = j0 / 32;
-    const int nvis = un.w - un.z;  // this unit's visits [v_begin, v_end) of the tile
-    (void)qmax;
-    const int64_t row_len = (int64_t)T * KT;
+    const int nvis = v_end - v_begin;  // this unit's visits [v_begin, v_end) of the tile
+    // per-lane part of the stage loads: row and swizzled chunk of each 16-byte piece
+    int drow[NDMA], dcol[NDMA];
+#pragma unroll
+    for (int u = 0; u < NDMA; ++u) {
+        const int e = wave * NCH + u * 64 + lane;
+        drow[u] = e / CPR;
+        dcol[u] = ((e % CPR) ^ row_swizzle<D>(e / CPR)) * 16;
+    }
+    const float* rowvec = wave < 4 ? lse2 : delta;
 
     // all of this wave's loads for one visit (32 positions x one query head)
     auto issue = [&](int vl, int stage) {
@@ -446,34 +461,96 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
         const int vi = v_begin + vl;
         const int i0 = (pb0 + vi / G) * 32;
         const int h = g * G + vi % G;
+        const int lim = N - 1 - i0;  // rows past the end repeat the last one
+        const int64_t base = (((int64_t)b * N + i0) * Hq + h) * D;
+        const __bf16* qb = q + base;
+        const __bf16* db = dout + base;
 #pragma unroll
         for (int u = 0; u < NDMA; ++u) {
             const int e0 = wave * NCH + u * 64;  // first chunk of this load
-            const int e = e0 + lane;
-            const int row = e / CPR;
-            const int gch = (e % CPR) ^ (row % CPR);
-            const int64_t off = (((int64_t)b * N + min(i0 + row, N - 1)) * Hq + h) * D + gch * 8;
+            const uint32_t off = (uint32_t)(min(drow[u], lim) * (Hq * D * 2) + dcol[u]);
             if (lane < NLANES) {
-                dma16(q + off, dst + e0 * 16);
-                dma16(dout + off, dst + NBYTES + e0 * 16);
+                dma16s(qb, off, dst + e0 * 16);
+                dma16s(db, off, dst + NBYTES + e0 * 16);
             }
         }
-        const int64_t tbase = ((int64_t)b * Hq + h) * D * row_len + i0;
+        const int ln = lane_id_here();
+        if (ln < 8) {
+            const float* rb = rowvec + ((int64_t)b * Hq + h) * N + i0;
+            dma4s(rb, (uint32_t)min((wave & 3) * 8 + ln, lim) * 4u, dst + 2 * NBYTES + wave * 32);
+        }
+    };
+
+    // one visit; FULL: every (query, key) pair of the block is visible
+    auto visit = [&](auto full_tag, const char* st, int i_lo) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const float* l2s = reinterpret_cast<const float*>(st + 2 * NBYTES);
+        const float* dls = l2s + 32;
+        // S = Q K^T, dP = dout V^T: 32 queries x this wave's 32 keys
+        f32x16 s, dp;
+        zero(s);
+        zero(dp);
+        // operand loads run one chunk ahead of the products; the scheduling
+        // fences stop the compiler from hoisting every load of the phase
+        // (which runs out of registers)
+        bf16x8 qa = ld16<bf16x8>(st + nat + nat_x), da = ld16<bf16x8>(st + NBYTES + nat + nat_x),
+               va = ld16<bf16x8>(vw + nat + nat_x);
 #pragma unroll
-        for (int u = 0; u < TDMA; ++u) {
-            const int e0 = wave * TCH + u * 64;
-            const int e = e0 + lane;
-            const int d = e / 4;
-            const int gsl = (e % 4) ^ ((d >> 2) & 3);
-            const int64_t off = tbase + (int64_t)d * row_len + gsl * 8;
-            if (lane < TLANES) {
-                dma16(qt + off, dst + 2 * NBYTES + e0 * 16);
-                dma16(dot + off, dst + 2 * NBYTES + TBYTES + e0 * 16);
+        for (int c = 0; c < NC; ++c) {
+            bf16x8 qn = qa, dn = da, vn = va;
+            if (c + 1 < NC) {
+                const int o = nat + ((32 * (c + 1)) ^ nat_x);
+                qn = ld16<bf16x8>(st + o);
+                dn = ld16<bf16x8>(st + NBYTES + o);
+                vn = ld16<bf16x8>(vw + o);
+            }
+            s = mfma32(qa, kf[c], s);
+            dp = mfma32(da, va, dp);
+            qa = qn;
+            da = dn;
+            va = vn;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 pbf[2], dsf[2];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int m0 = 8 * gq + 4 * hi;
+            const float4 l4 = *reinterpret_cast<const float4*>(l2s + m0);
+            const float4 d4 = *reinterpret_cast<const float4*>(dls + m0);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = gq * 4 + e;
+                float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -lv[e]));
+                if constexpr (!FULL) {
+                    const int i = i_lo + m0 + e;
+                    if (!(jk <= i && i <= sek)) p = 0.f;
+                }
+                pbf[r >> 3][r & 7] = (__bf16)p;
+                dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl[e]));
             }
         }
-        if (lane < 8) {
-            const int64_t roff = ((int64_t)b * Hq + h) * N + min(i0 + (wave & 3) * 8 + lane, N - 1);
-            dma4((wave < 4 ? lse : delta) + roff, dst + 2 * NBYTES + 2 * TBYTES + wave * 32);
+        __builtin_amdgcn_sched_barrier(0);
+        // dV^T += dout^T P, dK^T += Q^T dS (A operands by transposed loads,
+        // one (db, c2) step ahead of the products)
+        auto tr_pair = [&](int step, bf16x8& a_dv, bf16x8& a_dk) {
+            const int db = step >> 1, c2 = step & 1;
+            const char* r0 = st + c2 * 16 * NROW;
+            a_dv = ld_tr(r0 + NBYTES + tr_off[db][0], r0 + NBYTES + tr_off[db][1]);
+            a_dk = ld_tr(r0 + tr_off[db][0], r0 + tr_off[db][1]);
+        };
+        bf16x8 tv, tk;
+        tr_pair(0, tv, tk);
+#pragma unroll
+        for (int step = 0; step < 2 * NDB; ++step) {
+            bf16x8 nv = tv, nk = tk;
+            if (step + 1 < 2 * NDB) tr_pair(step + 1, nv, nk);
+            const int db = step >> 1, c2 = step & 1;
+            dvt[db] = mfma32(tv, pbf[c2], dvt[db]);
+            dkt[db] = mfma32(tk, dsf[c2], dkt[db]);
+            tv = nv;
+            tk = nk;
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -493,47 +570,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
         if (skip) continue;
         const bool full = (j0w + 31 <= i_lo) && (wmin >= i_lo + 31);
         const char* st = smem + (vi % NSTAGE) * STAGE;
-        const char* tq = st + 2 * NBYTES;
-        const char* td = tq + TBYTES;
-        const float* l2s = reinterpret_cast<const float*>(td + TBYTES);
-        const float* dls = l2s + 32;
-        // S = Q K^T, dP = dout V^T: 32 queries x this wave's 32 keys
-        f32x16 s, dp;
-        zero(s);
-        zero(dp);
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int o = l32 * NROW + (((hi + 2 * c) ^ (l32 % CPR)) * 16);
-            s = mfma32(ld16<bf16x8>(st + o), kf[c], s);
-            dp = mfma32(ld16<bf16x8>(st + NBYTES + o), vf[c], dp);
-        }
-        bf16x8 pbf[2], dsf[2];
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const int m0 = 8 * gq + 4 * hi;
-            const float4 l4 = *reinterpret_cast<const float4*>(l2s + m0);
-            const float4 d4 = *reinterpret_cast<const float4*>(dls + m0);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = gq * 4 + e;
-                const int i = i_lo + m0 + e;
-                float p = __builtin_amdgcn_exp2f(s[r] * scale_log2 - lv[e] * kLog2e);
-                if (!full && !(jk <= i && i <= sek)) p = 0.f;
-                pbf[r >> 3][r & 7] = (__bf16)p;
-                dsf[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl[e]));
-            }
-        }
-        // dV^T += dout^T P, dK^T += Q^T dS
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                const int d = db * 32 + l32;
-                const int o = d * TROW + (((c2 * 2 + hi) ^ ((d >> 2) & 3)) * 16);
-                dvt[db] = mfma32(ld16<bf16x8>(td + o), pbf[c2], dvt[db]);
-                dkt[db] = mfma32(ld16<bf16x8>(tq + o), dsf[c2], dkt[db]);
-            }
+        if (full) visit(std::true_type{}, st, i_lo);
+        else visit(std::false_type{}, st, i_lo);
     }
     if (kvalid && slot < 0) {
         __bf16* okp = dk + (((int64_t)b * N + jk) * Hkv + g) * D;
@@ -566,7 +604,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
                     make_float4(dvt[db][grp * 4], dvt[db][grp * 4 + 1], dvt[db][grp * 4 + 2], dvt[db][grp * 4 + 3]);
             }
     }
-    __syncthreads();  // unit_s and qmax_s are reused by the next unit
+    __syncthreads();  // unit_s is reused by the next unit
     }
 }
 
@@ -779,9 +817,9 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
 template <int D>
 hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
-    hipLaunchKernelGGL((bwd_prep<D>), dim3(T, a.Hq, a.B), dim3(256), 0, st, (const __bf16*)a.q, (const __bf16*)a.k,
-                       (const __bf16*)a.out, (const __bf16*)a.dout, a.se, a.N, a.Hq, a.Hkv, T, w.delta,
-                       (__bf16*)w.qt, (__bf16*)w.dot, (__bf16*)w.kt, w.tile_min, w.tile_max);
+    hipLaunchKernelGGL((bwd_prep<D>), dim3(T, a.Hq, a.B), dim3(256), 0, st, (const __bf16*)a.k,
+                       (const __bf16*)a.out, (const __bf16*)a.dout, a.lse, a.se, a.N, a.Hq, a.Hkv, T, w.delta,
+                       w.lse2, (__bf16*)w.kt, w.tile_min, w.tile_max);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_plan, dim3(1), dim3(1024), 0, st, w.tile_max, a.B, a.N, T, a.Hq / a.Hkv, a.Hkv, w.ctrl,
@@ -789,9 +827,9 @@ hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv<D>), dim3((unsigned)num_cus()), dim3(512), 0, st, (const __bf16*)a.q,
-                       (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, w.delta,
-                       (const __bf16*)w.qt, (const __bf16*)w.dot, a.se, a.B, a.N, a.Hq, a.Hkv, T, a.scale * kLog2e,
-                       a.scale, w.ctrl, w.units, w.partial, (__bf16*)a.dk, (__bf16*)a.dv);
+                       (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, w.lse2, w.delta, a.se, a.N,
+                       a.Hq, a.Hkv, a.scale * kLog2e, a.scale, w.ctrl, w.units, w.partial, (__bf16*)a.dk,
+                       (__bf16*)a.dv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_reduce<D>), dim3(kSplitSlots / 2, 8), dim3(256), 0, st, w.ctrl, w.split_tiles, w.partial,
@@ -821,8 +859,7 @@ size_t plan_bytes(int B, int N, int Hkv, int D) {
 size_t mfma_bwd_ws_bytes(int B, int N, int Hq, int Hkv, int D) {
     const size_t T = (size_t)(N + KT - 1) / KT;
     const size_t Np = T * KT;
-    return align256((size_t)B * Hq * N * sizeof(float)) + 2 * align256((size_t)B * Hq * D * Np * 2) +
-           align256((size_t)B * Hkv * D * Np * 2) + 2 * align256((size_t)B * T * sizeof(int32_t)) +
+    return 2 * align256((size_t)B * Hq * N * sizeof(float)) + align256((size_t)B * Hkv * D * Np * 2) + 2 * align256((size_t)B * T * sizeof(int32_t)) +
            plan_bytes(B, N, Hkv, D);
 }
 
@@ -833,10 +870,8 @@ BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D) {
     BwdWorkspace w;
     w.delta = reinterpret_cast<float*>(p);
     p += align256((size_t)B * Hq * N * sizeof(float));
-    w.qt = reinterpret_cast<uint16_t*>(p);
-    p += align256((size_t)B * Hq * D * Np * 2);
-    w.dot = reinterpret_cast<uint16_t*>(p);
-    p += align256((size_t)B * Hq * D * Np * 2);
+    w.lse2 = reinterpret_cast<float*>(p);
+    p += align256((size_t)B * Hq * N * sizeof(float));
     w.kt = reinterpret_cast<uint16_t*>(p);
     p += align256((size_t)B * Hkv * D * Np * 2);
     w.tile_min = reinterpret_cast<int32_t*>(p);

@@ -106,6 +106,26 @@ __device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
                  : "memory");
 }
 
+// Same loads from a wave-uniform base (an SGPR pair) plus a 32-bit per-lane
+// byte offset: the per-lane part of the address stays in one register.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, void* lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                 "s"(lds_addr(lds_base))
+                 : "memory");
+}
+__device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, void* lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr(lds_base))
+                 : "memory");
+}
+
+// Lane index recomputed where it is used (volatile: never hoisted or kept in
+// a register across a loop, where register pressure would spill it).
+__device__ __forceinline__ int lane_id_here() {
+    int r;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+    return r;
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt low bits [3:0], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
 template <int N>
