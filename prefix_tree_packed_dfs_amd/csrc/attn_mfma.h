@@ -17,18 +17,16 @@ inline bool mfma_supported(int D, int G) {
     return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G % 8 == 0);
 }
 
-// Workspace carved by the forward: per-tile subtree_end range and V transposed.
+// Workspace carved by the forward: per-tile subtree_end range.
 struct FwdWorkspace {
     int32_t* tile_min;   // [B, T]
     int32_t* tile_max;   // [B, T]
-    uint16_t* vt;        // bf16 bits [B, Hkv, D, T*KT], keys permuted inside each 16-key group
 };
 
 // Workspace carved by the backward.
 struct BwdWorkspace {
     float* delta;        // [B, Hq, N]  rowsum(dout * out)
     float* lse2;         // [B, Hq, N]  lse * log2(e)
-    uint16_t* kt;        // bf16 bits [B, Hkv, D, T*KT] K^T, rows permuted in 16-row groups
     int32_t* tile_min;   // [B, T]
     int32_t* tile_max;   // [B, T]
     // dK/dV work plan: KV tiles of 256 keys whose query range is long are split

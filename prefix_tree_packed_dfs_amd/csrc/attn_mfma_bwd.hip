@@ -53,20 +53,15 @@ int num_cus() {
 }
 
 // grid (T, Hq, B), 256 threads: delta and lse * log2(e) per (row, query
-// head), K^T per KV head (rows permuted in 16-row groups), and the per-tile
-// subtree_end range.
+// head), and the per-tile subtree_end range.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_prep(const __bf16* __restrict__ k, const __bf16* __restrict__ out,
-                                                const __bf16* __restrict__ dout, const float* __restrict__ lse,
-                                                const int32_t* __restrict__ se, int N, int Hq, int Hkv, int T,
-                                                float* __restrict__ delta, float* __restrict__ lse2,
-                                                __bf16* __restrict__ ktr, int32_t* __restrict__ tmin,
+__global__ __launch_bounds__(256) void bwd_prep(const __bf16* __restrict__ out, const __bf16* __restrict__ dout,
+                                                const float* __restrict__ lse, const int32_t* __restrict__ se,
+                                                int N, int Hq, int T, float* __restrict__ delta,
+                                                float* __restrict__ lse2, int32_t* __restrict__ tmin,
                                                 int32_t* __restrict__ tmax) {
-    constexpr int CPR = D / 8;
-    __shared__ __attribute__((aligned(16))) __bf16 ta[KT][D + 8];
     const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int j0 = t * KT;
-    const int64_t row_len = (int64_t)T * KT;
     {  // delta: four threads per row
         const int r = tid >> 2, part = tid & 3, j = j0 + r;
         float s = 0.f;
@@ -85,26 +80,6 @@ __global__ __launch_bounds__(256) void bwd_prep(const __bf16* __restrict__ k, co
             const int64_t ro = ((int64_t)b * Hq + h) * N + j;
             delta[ro] = s;
             lse2[ro] = lse[ro] * kLog2e;
-        }
-    }
-    if (h < Hkv) {  // K^T of KV head h
-        for (int e = tid; e < KT * CPR; e += 256) {
-            const int r = e / CPR, c = e % CPR, j = j0 + r;
-            bf16x8 vk = {};
-            if (j < N) vk = ld16<bf16x8>(k + (((int64_t)b * N + j) * Hkv + h) * D + c * 8);
-            *reinterpret_cast<bf16x8*>(&ta[r][c * 8]) = vk;
-        }
-        __syncthreads();
-        __bf16* dst_k = ktr + ((int64_t)b * Hkv + h) * D * row_len + j0;
-        for (int e = tid; e < D * (KT / 8); e += 256) {
-            const int d = e / (KT / 8), c = e % (KT / 8);
-            bf16x8 ok;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int p = c * 8 + u;
-                ok[u] = ta[(p >> 4) * 16 + inv_phys16(p & 15)][d];
-            }
-            *reinterpret_cast<bf16x8*>(dst_k + (int64_t)d * row_len + c * 8) = ok;
         }
     }
     if (h == 0 && tid < 64) {
@@ -616,29 +591,28 @@ template <int D, int HB>
 __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                  const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
                                                  const float* __restrict__ lse, const float* __restrict__ delta,
-                                                 const __bf16* __restrict__ ktr, const int32_t* __restrict__ se,
+                                                 const int32_t* __restrict__ se,
                                                  const int32_t* __restrict__ tmin, const int32_t* __restrict__ tmax,
                                                  int B, int N, int Hq, int Hkv, int T, int n_qtiles, int n_chunks,
                                                  float scale_log2, float scale, __bf16* __restrict__ dq) {
     constexpr int BM = 256 / HB;
     constexpr int NC = D / 16, NDB = D / 32;
     constexpr int CPR = D / 8;
-    constexpr int KROW = D * 2;            // natural K / V rows, swizzled
+    constexpr int KROW = D * 2;            // K / V rows as in memory, chunks swizzled by row_swizzle
     constexpr int KBYTES = KT * KROW;
-    constexpr int TROW = KT * 2;           // K^T rows, swizzled
-    constexpr int TBYTES = D * TROW;
-    constexpr int STAGE = 2 * KBYTES + TBYTES + KT * 4;
-    constexpr int NSTAGE = 3;
+    constexpr int STAGE = 2 * KBYTES + KT * 4;
+    constexpr int NSTAGE = 4;
     constexpr int KDMA = KBYTES / 1024 / 8;
-    constexpr int TDMA = TBYTES / 1024 / 8;
-    constexpr int PER_TILE = 2 * KDMA + TDMA + 1;
+    constexpr int PER_TILE = 2 * KDMA + 1;
+    static_assert(2 * PER_TILE < 16, "wait counts");
     constexpr int LCAP = 1024;
     constexpr int FULL = 1 << 30;
     __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
     __shared__ int list[LCAP];
     __shared__ int list_meta[2];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: load bases stay scalar
     const int l32 = lane & 31, hi = lane >> 5;
     const int GH = B * Hkv * n_chunks;
     const int gi = blockIdx.x % GH;
@@ -671,35 +645,51 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
         l2q = ip < N ? lse[((int64_t)b * Hq + head) * N + pc] * kLog2e : 0.f;
         dlq = ip < N ? delta[((int64_t)b * Hq + head) * N + pc] : 0.f;
     }
+    // these loads complete before any prefetch is issued, so the compiler's
+    // wait for them is not placed inside the tile loop (where it would drain
+    // the prefetches of later tiles)
+    wait_vmcnt<0>();
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) zero(acc[db]);
 
-    const int64_t row_len = (int64_t)T * KT;
-    const __bf16* ktb = ktr + ((int64_t)b * Hkv + g) * D * row_len;
-    const int64_t kvbase = ((int64_t)b * N * Hkv + g) * D;
-
+    const __bf16* kb_ = k + ((int64_t)b * N * Hkv + g) * D;
+    const __bf16* vb_ = v + ((int64_t)b * N * Hkv + g) * D;
+    int koff[KDMA], krow[KDMA];
+#pragma unroll
+    for (int u = 0; u < KDMA; ++u) {
+        const int kk = wave * KDMA + u;
+        krow[u] = kk * (64 / CPR) + lane / CPR;
+        koff[u] = ((lane % CPR) ^ row_swizzle<D>(krow[u])) * 16;
+    }
+    const int kstride = Hkv * D * 2;  // bytes between consecutive keys
     auto issue = [&](int t, int stage) {
         char* dst = smem + stage * STAGE;
         const int j0 = t * KT;
+        const int lim = N - 1 - j0;
+        const __bf16* kt = kb_ + (int64_t)j0 * Hkv * D;
+        const __bf16* vt = vb_ + (int64_t)j0 * Hkv * D;
 #pragma unroll
         for (int u = 0; u < KDMA; ++u) {
-            const int kk = wave * KDMA + u;
-            const int row = kk * (64 / CPR) + lane / CPR;
-            const int gch = (lane % CPR) ^ (row % CPR);
-            const int64_t off = kvbase + (int64_t)min(j0 + row, N - 1) * Hkv * D + gch * 8;
-            dma16(k + off, dst + kk * 1024);
-            dma16(v + off, dst + KBYTES + kk * 1024);
+            const uint32_t off = (uint32_t)(min(krow[u], lim) * kstride + koff[u]);
+            dma16s(kt, off, dst + (wave * KDMA + u) * 1024);
+            dma16s(vt, off, dst + KBYTES + (wave * KDMA + u) * 1024);
         }
-#pragma unroll
-        for (int u = 0; u < TDMA; ++u) {
-            const int kk = wave * TDMA + u;
-            const int d = kk * 8 + lane / 8;
-            const int gsl = (lane % 8) ^ ((d >> 1) & 7);
-            dma16(ktb + (int64_t)d * row_len + j0 + gsl * 8, dst + 2 * KBYTES + kk * 1024);
-        }
-        if (lane < 8) dma4(seb + min(j0 + wave * 8 + lane, N - 1), dst + 2 * KBYTES + TBYTES + wave * 32);
+        const int ln = lane_id_here();
+        if (ln < 8) dma4s(seb + j0, (uint32_t)min(wave * 8 + ln, lim) * 4u, dst + 2 * KBYTES + wave * 32);
     };
+    // operand loads of K / V rows: row x * 32 + l32, chunk 2c + hi
+    const int nat_x = (hi ^ row_swizzle<D>(l32)) * 16;
+    // transposed loads of K rows for the K^T operand (lane mapping as in the dK/dV kernel)
+    int tr_off[NDB][2];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int row = 4 * (lane >> 5) + ((lane >> 2) & 3) + 8 * half;
+            const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+            tr_off[db][half] = row * KROW + ((chunk ^ row_swizzle<D>(row)) * 16) + 8 * (lane & 1);
+        }
 
     int resume = 0;
     while (resume >= 0) {
@@ -728,20 +718,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
         const int cnt = list_meta[0];
         resume = list_meta[1];
 
-        if (cnt > 0) issue(list[0] & (FULL - 1), 0);
-        if (cnt > 1) issue(list[1] & (FULL - 1), 1);
+#pragma unroll
+        for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
+            if (s0 < cnt) issue(list[s0] & (FULL - 1), s0);
         for (int it = 0; it < cnt; ++it) {
-            if (it + 1 < cnt) wait_vmcnt<PER_TILE>();
+            // tiles issued after this one and possibly still in flight
+            const int ahead = min(cnt - 1 - it, NSTAGE - 2);
+            if (ahead >= 2) wait_vmcnt<2 * PER_TILE>();
+            else if (ahead == 1) wait_vmcnt<PER_TILE>();
             else wait_vmcnt<0>();
             barrier();
-            if (it + 2 < cnt) issue(list[it + 2] & (FULL - 1), (it + 2) % NSTAGE);
+            if (it + NSTAGE - 1 < cnt) issue(list[it + NSTAGE - 1] & (FULL - 1), (it + NSTAGE - 1) % NSTAGE);
             const int e = list[it];
             const int t = e & (FULL - 1);
             const bool full = (e & FULL) != 0;
             const int j0 = t * KT;
             const char* st = smem + (it % NSTAGE) * STAGE;
-            const char* tb = st + 2 * KBYTES;
-            const int* ses = reinterpret_cast<const int*>(tb + TBYTES);
+            const int* ses = reinterpret_cast<const int*>(st + 2 * KBYTES);
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 f32x16 sacc, dpt;
@@ -750,7 +743,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
                 const int row = x * 32 + l32;
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    const int o = row * KROW + (((hi + 2 * c) ^ (row % CPR)) * 16);
+                    const int o = row * KROW + ((32 * c) ^ nat_x);
                     sacc = mfma32(ld16<bf16x8>(st + o), qf[c], sacc);
                     dpt = mfma32(ld16<bf16x8>(st + KBYTES + o), df[c], dpt);
                 }
@@ -774,13 +767,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
                         dsf[r >> 3][r & 7] = (__bf16)(p * (dpt[r] - dlq));
                     }
                 }
+                // dQ^T += K^T dS^T (K^T by transposed loads of the K rows)
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
                     for (int c2 = 0; c2 < 2; ++c2) {
-                        const int d = db * 32 + l32;
-                        const bf16x8 a = ld16<bf16x8>(tb + d * TROW + (((x * 4 + c2 * 2 + hi) ^ ((d >> 1) & 7)) * 16));
-                        acc[db] = mfma32(a, dsf[c2], acc[db]);
+                        const char* r0 = st + (x * 32 + c2 * 16) * KROW;
+                        acc[db] = mfma32(ld_tr(r0 + tr_off[db][0], r0 + tr_off[db][1]), dsf[c2], acc[db]);
                     }
             }
         }
@@ -808,8 +801,8 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
     const int n_qtiles = (a.N + BM - 1) / BM;
     const int64_t blocks = (int64_t)n_qtiles * a.B * a.Hkv * n_chunks;
     hipLaunchKernelGGL((bwd_dq<D, HB>), dim3((unsigned)blocks), dim3(512), 0, st, (const __bf16*)a.q,
-                       (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, w.delta,
-                       (const __bf16*)w.kt, a.se, w.tile_min, w.tile_max, a.B, a.N, a.Hq, a.Hkv, T, n_qtiles,
+                       (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, w.delta, a.se,
+                       w.tile_min, w.tile_max, a.B, a.N, a.Hq, a.Hkv, T, n_qtiles,
                        n_chunks, a.scale * kLog2e, a.scale, (__bf16*)a.dq);
     return hipGetLastError();
 }
@@ -817,9 +810,8 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
 template <int D>
 hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
-    hipLaunchKernelGGL((bwd_prep<D>), dim3(T, a.Hq, a.B), dim3(256), 0, st, (const __bf16*)a.k,
-                       (const __bf16*)a.out, (const __bf16*)a.dout, a.lse, a.se, a.N, a.Hq, a.Hkv, T, w.delta,
-                       w.lse2, (__bf16*)w.kt, w.tile_min, w.tile_max);
+    hipLaunchKernelGGL((bwd_prep<D>), dim3(T, a.Hq, a.B), dim3(256), 0, st, (const __bf16*)a.out,
+                       (const __bf16*)a.dout, a.lse, a.se, a.N, a.Hq, T, w.delta, w.lse2, w.tile_min, w.tile_max);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_plan, dim3(1), dim3(1024), 0, st, w.tile_max, a.B, a.N, T, a.Hq / a.Hkv, a.Hkv, w.ctrl,
@@ -858,22 +850,18 @@ size_t plan_bytes(int B, int N, int Hkv, int D) {
 
 size_t mfma_bwd_ws_bytes(int B, int N, int Hq, int Hkv, int D) {
     const size_t T = (size_t)(N + KT - 1) / KT;
-    const size_t Np = T * KT;
-    return 2 * align256((size_t)B * Hq * N * sizeof(float)) + align256((size_t)B * Hkv * D * Np * 2) + 2 * align256((size_t)B * T * sizeof(int32_t)) +
+    return 2 * align256((size_t)B * Hq * N * sizeof(float)) + 2 * align256((size_t)B * T * sizeof(int32_t)) +
            plan_bytes(B, N, Hkv, D);
 }
 
 BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D) {
     const size_t T = (size_t)(N + KT - 1) / KT;
-    const size_t Np = T * KT;
     char* p = static_cast<char*>(ws);
     BwdWorkspace w;
     w.delta = reinterpret_cast<float*>(p);
     p += align256((size_t)B * Hq * N * sizeof(float));
     w.lse2 = reinterpret_cast<float*>(p);
     p += align256((size_t)B * Hq * N * sizeof(float));
-    w.kt = reinterpret_cast<uint16_t*>(p);
-    p += align256((size_t)B * Hkv * D * Np * 2);
     w.tile_min = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)B * T * sizeof(int32_t));
     w.tile_max = reinterpret_cast<int32_t*>(p);

@@ -21,9 +21,10 @@
 // In the 32x32 accumulator a lane holds one query (column) and 16 keys, so
 // the softmax reductions stay inside the lane except one exchange with lane
 // l^32, and the probabilities are already laid out as the B operand of the
-// next product.  V^T comes from a prep kernel that also permutes keys inside
-// each 16-key group to the order the accumulator holds them in, so each MFMA
-// operand is one 16-byte LDS read.  Online softmax in fp32 with exp2 and a
+// next product.  K and V tiles are staged in LDS as they are in memory
+// (16-byte chunks swizzled); the V^T operand comes from transposed LDS loads
+// (ds_read_b64_tr_b16) that also put the keys of each 16-key group in the
+// order the accumulator holds them.  Online softmax in fp32 with exp2 and a
 // log2(e)-prescaled scale; P is rounded to bf16 for the PV product.
 #include <climits>
 
@@ -36,50 +37,25 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994531f;
 
-// V -> V^T (keys permuted inside 16-key groups, zero past N) and per-tile
-// subtree_end range.  grid (T, Hkv, B), 256 threads.
-template <int D>
-__global__ __launch_bounds__(256) void fwd_prep(const __bf16* __restrict__ v, const int32_t* __restrict__ se,
-                                                int N, int Hkv, int T, int32_t* __restrict__ tmin,
-                                                int32_t* __restrict__ tmax, __bf16* __restrict__ vt) {
-    constexpr int CPR = D / 8;  // 16-byte chunks per key row
-    __shared__ __attribute__((aligned(16))) __bf16 tile[KT][D + 8];
-    const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-    const int j0 = t * KT;
-    for (int e = tid; e < KT * CPR; e += 256) {
-        const int r = e / CPR, c = e % CPR, j = j0 + r;
-        bf16x8 val = {};
-        if (j < N) val = *reinterpret_cast<const bf16x8*>(v + (((int64_t)b * N + j) * Hkv + g) * D + c * 8);
-        *reinterpret_cast<bf16x8*>(&tile[r][c * 8]) = val;
-    }
-    __syncthreads();
-    const int64_t row_len = (int64_t)T * KT;
-    __bf16* dst = vt + ((int64_t)b * Hkv + g) * D * row_len + j0;
-    for (int e = tid; e < D * (KT / 8); e += 256) {
-        const int d = e / (KT / 8), c = e % (KT / 8);
-        bf16x8 o;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int p = c * 8 + u;
-            o[u] = tile[(p >> 4) * 16 + inv_phys16(p & 15)][d];
-        }
-        *reinterpret_cast<bf16x8*>(dst + (int64_t)d * row_len + c * 8) = o;
-    }
-    if (g == 0 && tid < 64) {
-        const int j = j0 + tid;
-        const int s = j < N ? se[(int64_t)b * N + j] : -1;
-        const int mn = wave_min_i32(j < N ? s : INT_MAX);
-        const int mx = wave_max_i32(s);
-        if (tid == 0) {
-            tmin[(int64_t)b * T + t] = mn;
-            tmax[(int64_t)b * T + t] = mx;
-        }
+// Smallest and largest subtree_end of every 64-key tile: grid (ceil(T / 4), B),
+// 256 threads, one wave per tile.
+__global__ __launch_bounds__(256) void fwd_prep(const int32_t* __restrict__ se, int N, int T,
+                                                int32_t* __restrict__ tmin, int32_t* __restrict__ tmax) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6), b = blockIdx.y, lane = threadIdx.x & 63;
+    if (t >= T) return;
+    const int j = t * KT + lane;
+    const int s = j < N ? se[(int64_t)b * N + j] : -1;
+    const int mn = wave_min_i32(j < N ? s : INT_MAX);
+    const int mx = wave_max_i32(s);
+    if (lane == 0) {
+        tmin[(int64_t)b * T + t] = mn;
+        tmax[(int64_t)b * T + t] = mx;
     }
 }
 
 template <int D, int HB>
 __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                                                   const __bf16* __restrict__ vt, const int32_t* __restrict__ se,
+                                                   const __bf16* __restrict__ v, const int32_t* __restrict__ se,
                                                    const int32_t* __restrict__ tmin,
                                                    const int32_t* __restrict__ tmax, int B, int N, int Hq,
                                                    int Hkv, int T, int n_qtiles, int n_chunks, float scale_log2,
@@ -87,23 +63,21 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
     constexpr int BM = 256 / HB;          // positions per workgroup (8 waves x 32 rows = BM x HB)
     constexpr int NC = D / 16;            // 16-wide chunks of the head dim
     constexpr int NDB = D / 32;           // 32-row blocks of the head dim
-    constexpr int CPR = D / 8;            // 16-byte chunks per K row
-    constexpr int KROW = D * 2;           // LDS bytes per K row (16-byte chunks XOR-swizzled by row)
+    constexpr int CPR = D / 8;            // 16-byte chunks per K / V row
+    constexpr int KROW = D * 2;           // LDS bytes per row (chunks swizzled by row_swizzle)
     constexpr int KBYTES = KT * KROW;
-    constexpr int VROW = KT * 2;          // LDS bytes per V^T row (8 chunks, swizzled by row pair)
-    constexpr int VBYTES = D * VROW;
-    constexpr int STAGE = KBYTES + VBYTES + KT * 4;
+    constexpr int STAGE = 2 * KBYTES + KT * 4;
     constexpr int NSTAGE = 4;
-    constexpr int KDMA = KBYTES / 1024 / 8;   // 1 KB loads per wave per K tile
-    constexpr int VDMA = VBYTES / 1024 / 8;
-    constexpr int PER_TILE = KDMA + VDMA + 1; // vector memory ops per wave per tile
+    constexpr int KDMA = KBYTES / 1024 / 8;   // 1 KB loads per wave per K (and per V) tile
+    constexpr int PER_TILE = 2 * KDMA + 1;    // vector memory ops per wave per tile
     constexpr int LCAP = 1024;                // visible tiles listed per pass
     constexpr int FULL = 1 << 30;
     __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
     __shared__ int list[LCAP];
     __shared__ int list_meta[2];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: load bases stay scalar
     const int l32 = lane & 31, hi = lane >> 5;
     const int GH = B * Hkv * n_chunks;
     const int gi = blockIdx.x % GH;
@@ -132,45 +106,55 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
             qf[c] = ip < N ? *reinterpret_cast<const bf16x8*>(src + 16 * c) : z;
         }
     }
+    // Q completes before any prefetch is issued: the compiler's wait for it
+    // then does not drain the first tiles' prefetches
+    wait_vmcnt<0>();
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) zero(acc[db]);
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int64_t vt_row = (int64_t)T * KT;
-    const __bf16* vtb = vt + ((int64_t)b * Hkv + g) * D * vt_row;
     const __bf16* kb_ = k + ((int64_t)b * N * Hkv + g) * D;
+    const __bf16* vb_ = v + ((int64_t)b * N * Hkv + g) * D;
 
-    // all of this wave's loads of one tile: K rows (swizzled), V^T rows (swizzled),
+    // all of this wave's loads of one tile: K and V rows (swizzled) and
     // subtree_end.  Per-lane source offsets inside a tile are fixed, so they
     // are computed once; rows past the end of the row are clamped (last tile).
-    int koff[KDMA], krow[KDMA], voff[VDMA];
+    int koff[KDMA], krow[KDMA];
 #pragma unroll
     for (int u = 0; u < KDMA; ++u) {
         const int kk = wave * KDMA + u;
         krow[u] = kk * (64 / CPR) + lane / CPR;
-        koff[u] = ((lane % CPR) ^ (krow[u] % CPR)) * 8;
+        koff[u] = ((lane % CPR) ^ row_swizzle<D>(krow[u])) * 16;
     }
-#pragma unroll
-    for (int u = 0; u < VDMA; ++u) {
-        const int kk = wave * VDMA + u;
-        const int d = kk * 8 + lane / 8;
-        voff[u] = d * (int)vt_row + ((lane % 8) ^ ((d >> 1) & 7)) * 8;
-    }
-    const int64_t kstride = (int64_t)Hkv * D;
+    const int kstride = Hkv * D * 2;  // bytes between consecutive keys
     auto issue = [&](int t, int stage) {
         char* dst = smem + stage * STAGE;
         const int j0 = t * KT;
-        const bool tail = j0 + KT > N;
+        const int lim = N - 1 - j0;
+        const __bf16* kt = kb_ + (int64_t)j0 * Hkv * D;
+        const __bf16* vt = vb_ + (int64_t)j0 * Hkv * D;
 #pragma unroll
         for (int u = 0; u < KDMA; ++u) {
-            const int j = tail ? min(j0 + krow[u], N - 1) : j0 + krow[u];
-            dma16(kb_ + j * kstride + koff[u], dst + (wave * KDMA + u) * 1024);
+            const uint32_t off = (uint32_t)(min(krow[u], lim) * kstride + koff[u]);
+            dma16s(kt, off, dst + (wave * KDMA + u) * 1024);
+            dma16s(vt, off, dst + KBYTES + (wave * KDMA + u) * 1024);
         }
-#pragma unroll
-        for (int u = 0; u < VDMA; ++u) dma16(vtb + j0 + voff[u], dst + KBYTES + (wave * VDMA + u) * 1024);
-        if (lane < 8) dma4(seb + min(j0 + wave * 8 + lane, N - 1), dst + KBYTES + VBYTES + wave * 32);
+        const int ln = lane_id_here();
+        if (ln < 8) dma4s(seb + j0, (uint32_t)min(wave * 8 + ln, lim) * 4u, dst + 2 * KBYTES + wave * 32);
     };
+    // operand loads of K rows: row x * 32 + l32, chunk 2c + hi
+    const int nat_x = (hi ^ row_swizzle<D>(l32)) * 16;
+    // transposed loads of V rows (see the dK/dV kernel for the lane mapping)
+    int tr_off[NDB][2];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int row = 4 * (lane >> 5) + ((lane >> 2) & 3) + 8 * half;
+            const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+            tr_off[db][half] = row * KROW + ((chunk ^ row_swizzle<D>(row)) * 16) + 8 * (lane & 1);
+        }
 
     int resume = 0;
     while (resume >= 0) {
@@ -219,8 +203,7 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
                     const int row = x * 32 + l32;
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        st + row * KROW + (((hi + 2 * c) ^ (row % CPR)) * 16));
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + row * KROW + ((32 * c) ^ nat_x));
                     sacc[x] = c == 0 ? mfma32(a, qf[c], f32x16{}) : mfma32(a, qf[c], sacc[x]);
                 }
         };
@@ -245,7 +228,7 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
                 if (it + NSTAGE - 1 < cnt) issue(list[it + NSTAGE - 1] & (FULL - 1), (it + NSTAGE - 1) % NSTAGE);
             }
             if (!full) {
-                const int* ses = reinterpret_cast<const int*>(st + KBYTES + VBYTES);
+                const int* ses = reinterpret_cast<const int*>(st + 2 * KBYTES);
 #pragma unroll
                 for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -293,17 +276,15 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
                     pf[x][r >> 3][r & 7] = (__bf16)p;
                 }
             l_run += rs;
-            // O^T += V^T P^T
+            // O^T += V^T P^T (V^T by transposed loads of the V rows)
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int x = 0; x < 2; ++x)
 #pragma unroll
                     for (int c2 = 0; c2 < 2; ++c2) {
-                        const int d = db * 32 + l32;
-                        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                            st + KBYTES + d * VROW + (((x * 4 + c2 * 2 + hi) ^ ((d >> 1) & 7)) * 16));
-                        acc[db] = mfma32(a, pf[x][c2], acc[db]);
+                        const char* r0 = st + KBYTES + (x * 32 + c2 * 16) * KROW;
+                        acc[db] = mfma32(ld_tr(r0 + tr_off[db][0], r0 + tr_off[db][1]), pf[x][c2], acc[db]);
                     }
         }
         __syncthreads();  // the list is rebuilt only after every wave is done with it
@@ -336,7 +317,7 @@ hipError_t launch_main(const AttnArgs& a, const FwdWorkspace& w, int T, hipStrea
     const int64_t blocks = (int64_t)n_qtiles * a.B * a.Hkv * n_chunks;
     const float scale_log2 = a.scale * 1.4426950408889634f;
     hipLaunchKernelGGL((fwd_main<D, HB>), dim3((unsigned)blocks), dim3(512), 0, st, (const __bf16*)a.q,
-                       (const __bf16*)a.k, (const __bf16*)w.vt, a.se, w.tile_min, w.tile_max, a.B, a.N, a.Hq,
+                       (const __bf16*)a.k, (const __bf16*)a.v, a.se, w.tile_min, w.tile_max, a.B, a.N, a.Hq,
                        a.Hkv, T, n_qtiles, n_chunks, scale_log2, (__bf16*)a.out, a.lse);
     return hipGetLastError();
 }
@@ -344,8 +325,7 @@ hipError_t launch_main(const AttnArgs& a, const FwdWorkspace& w, int T, hipStrea
 template <int D>
 hipError_t launch_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
-    hipLaunchKernelGGL((fwd_prep<D>), dim3(T, a.Hkv, a.B), dim3(256), 0, st, (const __bf16*)a.v, a.se, a.N, a.Hkv,
-                       T, w.tile_min, w.tile_max, (__bf16*)w.vt);
+    hipLaunchKernelGGL(fwd_prep, dim3((T + 3) / 4, a.B), dim3(256), 0, st, a.se, a.N, T, w.tile_min, w.tile_max);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     switch (heads_per_wg(a.Hq / a.Hkv)) {
@@ -361,21 +341,21 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
 size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D) {
+    (void)Hkv;
+    (void)D;
     const size_t T = (size_t)(N + KT - 1) / KT;
-    return 2 * align256((size_t)B * T * sizeof(int32_t)) + align256((size_t)B * Hkv * D * T * KT * 2);
+    return 2 * align256((size_t)B * T * sizeof(int32_t));
 }
 
 FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D) {
+    (void)Hkv;
+    (void)D;
     const size_t T = (size_t)(N + KT - 1) / KT;
     char* p = static_cast<char*>(ws);
     FwdWorkspace w;
     w.tile_min = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)B * T * sizeof(int32_t));
     w.tile_max = reinterpret_cast<int32_t*>(p);
-    p += align256((size_t)B * T * sizeof(int32_t));
-    w.vt = reinterpret_cast<uint16_t*>(p);
-    (void)Hkv;
-    (void)D;
     return w;
 }
 
