@@ -42,6 +42,8 @@ struct BwdWorkspace {
 constexpr int kSplitSlots = 1536;
 constexpr int kVisitBudget = 96;
 
+// Smallest and largest subtree_end of every KT-key tile of each row ([B, T]).
+hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, int32_t* tmax, hipStream_t st);
 size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D);
 FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D);
 hipError_t mfma_attn_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st);

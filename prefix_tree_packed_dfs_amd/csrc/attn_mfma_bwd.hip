@@ -52,45 +52,34 @@ int num_cus() {
     return cached[dev];
 }
 
-// grid (T, Hq, B), 256 threads: delta and lse * log2(e) per (row, query
-// head), and the per-tile subtree_end range.
+// delta = rowsum(dout * out) and lse * log2(e) for every (row, position,
+// query head), stored [B, Hq, N].  D / 16 threads per (b, j, h) row of out and
+// dout, 16 elements each, so a wave reads contiguous memory.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep(const __bf16* __restrict__ out, const __bf16* __restrict__ dout,
-                                                const float* __restrict__ lse, const int32_t* __restrict__ se,
-                                                int N, int Hq, int T, float* __restrict__ delta,
-                                                float* __restrict__ lse2, int32_t* __restrict__ tmin,
-                                                int32_t* __restrict__ tmax) {
-    const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-    const int j0 = t * KT;
-    {  // delta: four threads per row
-        const int r = tid >> 2, part = tid & 3, j = j0 + r;
-        float s = 0.f;
-        if (j < N) {
-            const int64_t off = (((int64_t)b * N + j) * Hq + h) * D + part * (D / 4);
+                                                const float* __restrict__ lse, int N, int Hq, int64_t rows,
+                                                float* __restrict__ delta, float* __restrict__ lse2) {
+    constexpr int TPR = D / 16;
+    const int64_t r = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    const int part = threadIdx.x % TPR;
+    float s = 0.f;
+    if (r < rows) {
+        const int64_t off = r * D + part * 16;
 #pragma unroll
-            for (int c = 0; c < D / 4; c += 8) {
-                const bf16x8 a = ld16<bf16x8>(out + off + c), d8 = ld16<bf16x8>(dout + off + c);
+        for (int c = 0; c < 16; c += 8) {
+            const bf16x8 a = ld16<bf16x8>(out + off + c), d8 = ld16<bf16x8>(dout + off + c);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) s = fmaf((float)a[u], (float)d8[u], s);
-            }
-        }
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        if (part == 0 && j < N) {
-            const int64_t ro = ((int64_t)b * Hq + h) * N + j;
-            delta[ro] = s;
-            lse2[ro] = lse[ro] * kLog2e;
+            for (int u = 0; u < 8; ++u) s = fmaf((float)a[u], (float)d8[u], s);
         }
     }
-    if (h == 0 && tid < 64) {
-        const int j = j0 + tid;
-        const int s = j < N ? se[(int64_t)b * N + j] : -1;
-        const int mn = wave_min_i32(j < N ? s : INT_MAX);
-        const int mx = wave_max_i32(s);
-        if (tid == 0) {
-            tmin[(int64_t)b * T + t] = mn;
-            tmax[(int64_t)b * T + t] = mx;
-        }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) s += __shfl_xor(s, o, 64);
+    if (part == 0 && r < rows) {
+        const int h = (int)(r % Hq);
+        const int64_t bj = r / Hq;
+        const int64_t ro = ((bj / N) * Hq + h) * N + bj % N;
+        delta[ro] = s;
+        lse2[ro] = lse[ro] * kLog2e;
     }
 }
 
@@ -731,7 +720,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
             if (it + NSTAGE - 1 < cnt) issue(list[it + NSTAGE - 1] & (FULL - 1), (it + NSTAGE - 1) % NSTAGE);
             const int e = list[it];
             const int t = e & (FULL - 1);
-            const bool full = (e & FULL) != 0;
+            const bool full = __builtin_amdgcn_readfirstlane(e & FULL) != 0;
             const int j0 = t * KT;
             const char* st = smem + (it % NSTAGE) * STAGE;
             const int* ses = reinterpret_cast<const int*>(st + 2 * KBYTES);
@@ -746,27 +735,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
                     const int o = row * KROW + ((32 * c) ^ nat_x);
                     sacc = mfma32(ld16<bf16x8>(st + o), qf[c], sacc);
                     dpt = mfma32(ld16<bf16x8>(st + KBYTES + o), df[c], dpt);
+                    if (c % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+                }
+                float p[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -l2q));
+                if (!full) {  // the interval test, only on tiles that are not fully visible
+                    asm volatile("");  // keep this a branch (not selects run on every tile)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int jj = x * 32 + 8 * gq + 4 * hi;
+                        const int4 s4 = *reinterpret_cast<const int4*>(ses + jj);
+                        const int sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+                        for (int e4 = 0; e4 < 4; ++e4)
+                            if (!(j0 + jj + e4 <= ip && ip <= sv[e4])) p[gq * 4 + e4] = 0.f;
+                    }
                 }
                 bf16x8 dsf[2];
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const int jj = x * 32 + 8 * gq + 4 * hi;
-                    int sv[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
-                    if (!full) {
-                        const int4 s4 = *reinterpret_cast<const int4*>(ses + jj);
-                        sv[0] = s4.x;
-                        sv[1] = s4.y;
-                        sv[2] = s4.z;
-                        sv[3] = s4.w;
-                    }
-#pragma unroll
-                    for (int e4 = 0; e4 < 4; ++e4) {
-                        const int r = gq * 4 + e4;
-                        float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -l2q));
-                        if (!full && !(j0 + jj + e4 <= ip && ip <= sv[e4])) p = 0.f;
-                        dsf[r >> 3][r & 7] = (__bf16)(p * (dpt[r] - dlq));
-                    }
-                }
+                for (int r = 0; r < 16; ++r) dsf[r >> 3][r & 7] = (__bf16)(p[r] * (dpt[r] - dlq));
                 // dQ^T += K^T dS^T (K^T by transposed loads of the K rows)
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
@@ -775,6 +763,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
                         const char* r0 = st + (x * 32 + c2 * 16) * KROW;
                         acc[db] = mfma32(ld_tr(r0 + tr_off[db][0], r0 + tr_off[db][1]), dsf[c2], acc[db]);
                     }
+                // keep the two key halves apart: interleaving them needs more
+                // registers than a wave has
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         __syncthreads();
@@ -810,9 +801,13 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
 template <int D>
 hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
-    hipLaunchKernelGGL((bwd_prep<D>), dim3(T, a.Hq, a.B), dim3(256), 0, st, (const __bf16*)a.out,
-                       (const __bf16*)a.dout, a.lse, a.se, a.N, a.Hq, T, w.delta, w.lse2, w.tile_min, w.tile_max);
+    const int64_t rows = (int64_t)a.B * a.N * a.Hq;
+    constexpr int RPB = 256 / (D / 16);  // rows per block
+    hipLaunchKernelGGL((bwd_prep<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
+                       (const __bf16*)a.out, (const __bf16*)a.dout, a.lse, a.N, a.Hq, rows, w.delta, w.lse2);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_plan, dim3(1), dim3(1024), 0, st, w.tile_max, a.B, a.N, T, a.Hq / a.Hkv, a.Hkv, w.ctrl,
                        w.tile_plan, w.units, w.split_tiles);

@@ -266,7 +266,7 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
             // probabilities of this tile, and its PV product.
             s_product(smem + ((more ? it + 1 : it) % NSTAGE) * STAGE, snext);
             bf16x8 pf[2][2];
-            float rs = 0.f;
+            float rs = 0.f;  // fp32 row sum of the unrounded probabilities
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -325,8 +325,7 @@ hipError_t launch_main(const AttnArgs& a, const FwdWorkspace& w, int T, hipStrea
 template <int D>
 hipError_t launch_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
-    hipLaunchKernelGGL(fwd_prep, dim3((T + 3) / 4, a.B), dim3(256), 0, st, a.se, a.N, T, w.tile_min, w.tile_max);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, st);
     if (e != hipSuccess) return e;
     switch (heads_per_wg(a.Hq / a.Hkv)) {
         case 1: return launch_main<D, 1>(a, w, T, st);
@@ -357,6 +356,12 @@ FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D) {
     p += align256((size_t)B * T * sizeof(int32_t));
     w.tile_max = reinterpret_cast<int32_t*>(p);
     return w;
+}
+
+hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, int32_t* tmax, hipStream_t st) {
+    const int T = (N + KT - 1) / KT;
+    hipLaunchKernelGGL(fwd_prep, dim3((T + 3) / 4, B), dim3(256), 0, st, se, N, T, tmin, tmax);
+    return hipGetLastError();
 }
 
 hipError_t mfma_attn_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st) {
