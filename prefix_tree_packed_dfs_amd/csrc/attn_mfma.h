@@ -32,14 +32,16 @@ struct BwdWorkspace {
     // dK/dV work plan: KV tiles of 256 keys whose query range is long are split
     // into chunks of visits; chunks write fp32 partials that a reduce pass sums
     int32_t* ctrl;       // queue counters / lengths / starts, split-tile count
-    int4* tile_plan;     // [B * T256] {first query block, last query block, chunks, first slot or -1}
+    int4* tile_plan;     // [B * TT] {first query block, last query block, chunks, first slot or -1}
     int4* units;         // [unit capacity][2] {b*Hkv+g, tile, first visit, end visit}, {slot, 0, 0, 0}
     int4* split_tiles;   // [kSplitSlots/2] {b, tile, first slot, splits}
-    float* partial;      // [kSplitSlots][2][256][D] fp32 dK, dV partial sums
+    float* partial;      // [kSplitSlots][2][kKvTile][D] fp32 dK, dV partial sums
 };
 
-// Partial-sum slots for split dK/dV tiles, and the initial visit budget per chunk.
-constexpr int kSplitSlots = 1536;
+// Keys per dK/dV workgroup tile, partial-sum slots for split tiles, and the
+// initial visit budget per chunk.
+constexpr int kKvTile = 256;
+constexpr int kSplitSlots = 1536 * 256 / kKvTile;
 constexpr int kVisitBudget = 96;
 
 // Smallest and largest subtree_end of every KT-key tile of each row ([B, T]).

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void bwd_prep(const __bf16* __restrict__ out, 
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV work plan (one workgroup).  A KV tile of 256 keys visits every
+// dK/dV work plan (one workgroup).  A KV tile of kKvTile keys visits every
 // (32-position block, query head) pair from its first key's block to the
 // block of the largest subtree_end among its keys.  Keys of a long shared
 // prefix visit almost the whole row while keys near the leaves visit a few
@@ -122,15 +122,16 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
     __shared__ int s_scan[1024];
     __shared__ int s_cnt[kPlanBuckets];
     const int tid = threadIdx.x;
-    const int T256 = (N + 255) / 256;
-    const int BT = B * T256;
+    const int TT = (N + kKvTile - 1) / kKvTile;  // KV tiles per row
+    const int BT = B * TT;
+    constexpr int SUB = kKvTile / KT, BPT = kKvTile / 32;  // 64-key tiles, 32-key blocks per KV tile
     const int NB = (N + 31) / 32;
     const int NQ = Hkv < 8 ? Hkv : 8;
     for (int u = tid; u < BT; u += 1024) {
-        const int b = u / T256, t = u % T256;
+        const int b = u / TT, t = u % TT;
         int qmax = -1;
-        for (int x = 4 * t; x < min(4 * t + 4, T); ++x) qmax = max(qmax, tmax[(int64_t)b * T + x]);
-        tile_plan[u] = make_int4(8 * t, max(qmax / 32, 8 * t), 1, -1);
+        for (int x = SUB * t; x < min(SUB * t + SUB, T); ++x) qmax = max(qmax, tmax[(int64_t)b * T + x]);
+        tile_plan[u] = make_int4(BPT * t, max(qmax / 32, BPT * t), 1, -1);
     }
     if (tid == 0) s_budget = kVisitBudget;
     __syncthreads();
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
             if (nc > 1) {
                 e.z = nc;
                 e.w = slot;
-                split_tiles[z] = make_int4(u / T256, u % T256, slot, nc);
+                split_tiles[z] = make_int4(u / TT, u % TT, slot, nc);
                 slot += nc;
                 ++z;
             }
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
     __syncthreads();
     for (int u = u0; u < u1; ++u) {
         const int4 e = tile_plan[u];
-        const int kb = (u / T256) * NBK + e.x / C;
+        const int kb = (u / TT) * NBK + e.x / C;
         for (int kk = 0; kk < e.z; ++kk) atomicAdd(&s_cnt[(kb + kk) >> shift], 1);
     }
     __syncthreads();
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
     __syncthreads();
     for (int u = u0; u < u1; ++u) {
         const int4 e = tile_plan[u];
-        const int b = u / T256, t = u % T256;
+        const int b = u / TT, t = u % TT;
         const int kb = b * NBK + e.x / C;
         for (int kk = 0; kk < e.z; ++kk) {
             const int pos = atomicAdd(&s_cnt[(kb + kk) >> shift], 1);
@@ -263,9 +264,9 @@ __global__ __launch_bounds__(256) void bwd_reduce(const int* __restrict__ ctrl,
     if (w >= n_split * Hkv) return;
     const int4 st = split_tiles[w / Hkv];
     const int g = w % Hkv;
-    const int b = st.x, j0 = st.y * 256;
+    const int b = st.x, j0 = st.y * kKvTile;
     const int k0 = blockIdx.y * 32;
-    constexpr int SLOT = 2 * 256 * D;  // floats per slot
+    constexpr int SLOT = 2 * kKvTile * D;  // floats per slot
     for (int e = threadIdx.x; e < 2 * 32 * D / 4; e += 256) {
         const int which = e / (32 * D / 4);           // 0: dK, 1: dV
         const int rem = e % (32 * D / 4);
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(256) void bwd_reduce(const int* __restrict__ ctrl,
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int kk = 0; kk < st.w; ++kk) {
             const float4 v = *reinterpret_cast<const float4*>(
-                partial + (int64_t)((st.z + kk) * Hkv + g) * SLOT + which * 256 * D + kl * D + d4 * 4);
+                partial + (int64_t)((st.z + kk) * Hkv + g) * SLOT + which * kKvTile * D + kl * D + d4 * 4);
             acc.x += v.x;
             acc.y += v.y;
             acc.z += v.z;
@@ -364,7 +365,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
     const int slot = __builtin_amdgcn_readfirstlane(unit_s[1].x);
     if (ux < 0) break;
     const int g = ux % Hkv, b = ux / Hkv;
-    const int j0 = __builtin_amdgcn_readfirstlane(unit_s[0].y) * 256;
+    static_assert(kKvTile == 256, "eight waves of 32 keys");
+    const int j0 = __builtin_amdgcn_readfirstlane(unit_s[0].y) * kKvTile;
     const int v_begin = __builtin_amdgcn_readfirstlane(unit_s[0].z);
     const int v_end = __builtin_amdgcn_readfirstlane(unit_s[0].w);
     const int j0w = j0 + 32 * wave;
@@ -554,8 +556,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
                 *reinterpret_cast<bf16x4*>(ovp + db * 32 + grp * 8 + hi * 4) = b4;
             }
     } else if (slot >= 0) {  // a chunk of a split tile: fp32 partials, summed by bwd_reduce
-        float* pk = partial + (int64_t)slot * 2 * 256 * D + (32 * wave + l32) * D;
-        float* pv = pk + 256 * D;
+        float* pk = partial + (int64_t)slot * 2 * kKvTile * D + (32 * wave + l32) * D;
+        float* pv = pk + kKvTile * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -819,7 +821,7 @@ hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) 
                        (__bf16*)a.dv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_reduce<D>), dim3(kSplitSlots / 2, 8), dim3(256), 0, st, w.ctrl, w.split_tiles, w.partial,
+    hipLaunchKernelGGL((bwd_reduce<D>), dim3(kSplitSlots / 2, kKvTile / 32), dim3(256), 0, st, w.ctrl, w.split_tiles, w.partial,
                        a.N, a.Hkv, (__bf16*)a.dk, (__bf16*)a.dv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -834,11 +836,11 @@ hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 size_t plan_bytes(int B, int N, int Hkv, int D) {
-    const size_t T256 = (size_t)(N + 255) / 256;
-    const size_t ucap = (size_t)kSplitSlots + (size_t)B * T256 * Hkv;
-    return align256(32 * sizeof(int)) + align256((size_t)B * T256 * sizeof(int4)) +
+    const size_t TT = (size_t)(N + kKvTile - 1) / kKvTile;
+    const size_t ucap = (size_t)kSplitSlots + (size_t)B * TT * Hkv;
+    return align256(32 * sizeof(int)) + align256((size_t)B * TT * sizeof(int4)) +
            align256(ucap * 2 * sizeof(int4)) + align256((size_t)(kSplitSlots / 2) * sizeof(int4)) +
-           align256((size_t)kSplitSlots * 2 * 256 * D * sizeof(float));
+           align256((size_t)kSplitSlots * 2 * kKvTile * D * sizeof(float));
 }
 
 }  // namespace
@@ -861,12 +863,12 @@ BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D) {
     p += align256((size_t)B * T * sizeof(int32_t));
     w.tile_max = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)B * T * sizeof(int32_t));
-    const size_t T256 = (size_t)(N + 255) / 256;
-    const size_t ucap = (size_t)kSplitSlots + (size_t)B * T256 * Hkv;
+    const size_t TT = (size_t)(N + kKvTile - 1) / kKvTile;
+    const size_t ucap = (size_t)kSplitSlots + (size_t)B * TT * Hkv;
     w.ctrl = reinterpret_cast<int32_t*>(p);
     p += align256(32 * sizeof(int));
     w.tile_plan = reinterpret_cast<int4*>(p);
-    p += align256((size_t)B * T256 * sizeof(int4));
+    p += align256((size_t)B * TT * sizeof(int4));
     w.units = reinterpret_cast<int4*>(p);
     p += align256(ucap * 2 * sizeof(int4));
     w.split_tiles = reinterpret_cast<int4*>(p);
