@@ -5,21 +5,21 @@
 // P = exp(scale * q.k - lse) and delta_i = dout_i . out_i:
 //   dV = P^T dout,   dP = dout V^T,   dS = P * (dP - delta),
 //   dK = scale dS^T Q,   dQ = scale dS K.
-// Three kernels, no atomics (the result is bitwise reproducible):
-//   bwd_prep  delta, Q^T and dout^T per query head, K^T per KV head (rows
-//             permuted in 16-row groups to match the accumulator order), and
-//             the per-tile subtree_end range;
-//   bwd_dkdv  KV-stationary: a workgroup owns 128 keys of one KV head (32 per
-//             wave, K and V held as MFMA operands in registers) and walks the
-//             query blocks [j0, max subtree_end] for every query head of the
-//             group.  A wave skips a 32x32 block whose keys see none of its
-//             queries and drops the mask where all of them are visible.
-//               S = Q K^T, dP = dout V^T     (A = Q, dout from LDS)
-//               dV^T += dout^T P, dK^T += Q^T dS   (B = P, dS straight from
-//               the S / dP accumulators: a lane holds one key and 16 queries)
-//   bwd_dq    query-stationary, shaped like the forward: S^T = K Q^T and
-//             dP^T = V dout^T with Q, dout in registers, then
-//             dQ^T += K^T dS^T with dS^T taken from the accumulator.
+// Kernels, in launch order, no atomics on results (bitwise reproducible):
+//   tile ranges  min / max subtree_end per 64-key tile (shared with the
+//                forward);
+//   bwd_plan     the dK/dV work plan (split long KV tiles, per-XCD queues);
+//   bwd_dq       query-stationary, shaped like the forward: S^T = K Q^T and
+//                dP^T = V dout^T with Q, dout in registers, then
+//                dQ^T += K^T dS^T with dS^T taken from the accumulator; it
+//                also writes delta and lse * log2(e) for the next kernel;
+//   bwd_dkdv     KV-stationary and persistent: a workgroup owns 256 keys of
+//                one KV head (32 per wave) and walks the query blocks its
+//                keys can see, for every query head of the group:
+//                  S = Q K^T, dP = dout V^T     (A = Q, dout rows from LDS)
+//                  dV^T += dout^T P, dK^T += Q^T dS   (A by transposed LDS
+//                  loads, B = P, dS straight from the S / dP accumulators)
+//   bwd_reduce   sums the partials of split tiles in chunk order.
 // dK/dV and dQ recompute S and dP separately (7 products instead of 5) so
 // that no partial dQ has to be summed across workgroups.
 #include <climits>
@@ -50,37 +50,6 @@ int num_cus() {
         cached[dev] = n;
     }
     return cached[dev];
-}
-
-// delta = rowsum(dout * out) and lse * log2(e) for every (row, position,
-// query head), stored [B, Hq, N].  D / 16 threads per (b, j, h) row of out and
-// dout, 16 elements each, so a wave reads contiguous memory.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep(const __bf16* __restrict__ out, const __bf16* __restrict__ dout,
-                                                const float* __restrict__ lse, int N, int Hq, int64_t rows,
-                                                float* __restrict__ delta, float* __restrict__ lse2) {
-    constexpr int TPR = D / 16;
-    const int64_t r = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-    const int part = threadIdx.x % TPR;
-    float s = 0.f;
-    if (r < rows) {
-        const int64_t off = r * D + part * 16;
-#pragma unroll
-        for (int c = 0; c < 16; c += 8) {
-            const bf16x8 a = ld16<bf16x8>(out + off + c), d8 = ld16<bf16x8>(dout + off + c);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) s = fmaf((float)a[u], (float)d8[u], s);
-        }
-    }
-#pragma unroll
-    for (int o = 1; o < TPR; o <<= 1) s += __shfl_xor(s, o, 64);
-    if (part == 0 && r < rows) {
-        const int h = (int)(r % Hq);
-        const int64_t bj = r / Hq;
-        const int64_t ro = ((bj / N) * Hq + h) * N + bj % N;
-        delta[ro] = s;
-        lse2[ro] = lse[ro] * kLog2e;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -580,8 +549,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
 // ---------------------------------------------------------------------------
 template <int D, int HB>
 __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                                                 const __bf16* __restrict__ v, const __bf16* __restrict__ dout,
-                                                 const float* __restrict__ lse, const float* __restrict__ delta,
+                                                 const __bf16* __restrict__ v, const __bf16* __restrict__ out,
+                                                 const __bf16* __restrict__ dout, const float* __restrict__ lse,
+                                                 float* __restrict__ delta, float* __restrict__ lse2,
                                                  const int32_t* __restrict__ se,
                                                  const int32_t* __restrict__ tmin, const int32_t* __restrict__ tmax,
                                                  int B, int N, int Hq, int Hkv, int T, int n_qtiles, int n_chunks,
@@ -622,19 +592,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
     const int32_t* seb = se + (int64_t)b * N;
     const int ip = i0 + (wave / HB) * 32 + l32;
 
+    // Q and dout of this lane's query in registers (lane halves hold the two
+    // halves of each 16-wide chunk of the head dim); delta = dout . out of the
+    // query is a dot over both halves, and it and lse * log2(e) are stored
+    // for the dK/dV kernel, which runs after this one.
     bf16x8 qf[NC], df[NC];
     float l2q, dlq;
     {
         const int pc = min(ip, N - 1);
         const int64_t off = (((int64_t)b * N + pc) * Hq + head) * D + hi * 8;
+        float dot = 0.f;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            bf16x8 z = {};
-            qf[c] = ip < N ? ld16<bf16x8>(q + off + 16 * c) : z;
-            df[c] = ip < N ? ld16<bf16x8>(dout + off + 16 * c) : z;
+            qf[c] = ld16<bf16x8>(q + off + 16 * c);
+            df[c] = ld16<bf16x8>(dout + off + 16 * c);
+            const bf16x8 of = ld16<bf16x8>(out + off + 16 * c);
+            const bf16x8 d8 = df[c];
+            dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(of, of, 0, 1),
+                                                  __builtin_shufflevector(d8, d8, 0, 1), dot, false);
+            dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(of, of, 2, 3),
+                                                  __builtin_shufflevector(d8, d8, 2, 3), dot, false);
+            dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(of, of, 4, 5),
+                                                  __builtin_shufflevector(d8, d8, 4, 5), dot, false);
+            dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(of, of, 6, 7),
+                                                  __builtin_shufflevector(d8, d8, 6, 7), dot, false);
         }
-        l2q = ip < N ? lse[((int64_t)b * Hq + head) * N + pc] * kLog2e : 0.f;
-        dlq = ip < N ? delta[((int64_t)b * Hq + head) * N + pc] : 0.f;
+        const int64_t ro = ((int64_t)b * Hq + head) * N + pc;
+        l2q = lse[ro] * kLog2e;
+        dlq = add_xor32(dot);
+        if (ip < N && hi == 0) {
+            delta[ro] = dlq;
+            lse2[ro] = l2q;
+        }
     }
     // these loads complete before any prefetch is issued, so the compiler's
     // wait for them is not placed inside the tile loop (where it would drain
@@ -794,7 +783,8 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
     const int n_qtiles = (a.N + BM - 1) / BM;
     const int64_t blocks = (int64_t)n_qtiles * a.B * a.Hkv * n_chunks;
     hipLaunchKernelGGL((bwd_dq<D, HB>), dim3((unsigned)blocks), dim3(512), 0, st, (const __bf16*)a.q,
-                       (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse, w.delta, a.se,
+                       (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.out, (const __bf16*)a.dout, a.lse,
+                       w.delta, w.lse2, a.se,
                        w.tile_min, w.tile_max, a.B, a.N, a.Hq, a.Hkv, T, n_qtiles,
                        n_chunks, a.scale * kLog2e, a.scale, (__bf16*)a.dq);
     return hipGetLastError();
@@ -803,17 +793,19 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
 template <int D>
 hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
-    const int64_t rows = (int64_t)a.B * a.N * a.Hq;
-    constexpr int RPB = 256 / (D / 16);  // rows per block
-    hipLaunchKernelGGL((bwd_prep<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
-                       (const __bf16*)a.out, (const __bf16*)a.dout, a.lse, a.N, a.Hq, rows, w.delta, w.lse2);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, st);
+    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_plan, dim3(1), dim3(1024), 0, st, w.tile_max, a.B, a.N, T, a.Hq / a.Hkv, a.Hkv, w.ctrl,
                        w.tile_plan, w.units, w.split_tiles);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // dQ first: it also writes delta and lse * log2(e), which dK/dV reads
+    switch (heads_per_wg(a.Hq / a.Hkv)) {
+        case 1: e = launch_dq<D, 1>(a, w, T, st); break;
+        case 2: e = launch_dq<D, 2>(a, w, T, st); break;
+        case 4: e = launch_dq<D, 4>(a, w, T, st); break;
+        default: e = launch_dq<D, 8>(a, w, T, st); break;
+    }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv<D>), dim3((unsigned)num_cus()), dim3(512), 0, st, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, w.lse2, w.delta, a.se, a.N,
@@ -821,16 +813,9 @@ hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) 
                        (__bf16*)a.dv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_reduce<D>), dim3(kSplitSlots / 2, kKvTile / 32), dim3(256), 0, st, w.ctrl, w.split_tiles, w.partial,
-                       a.N, a.Hkv, (__bf16*)a.dk, (__bf16*)a.dv);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    switch (heads_per_wg(a.Hq / a.Hkv)) {
-        case 1: return launch_dq<D, 1>(a, w, T, st);
-        case 2: return launch_dq<D, 2>(a, w, T, st);
-        case 4: return launch_dq<D, 4>(a, w, T, st);
-        default: return launch_dq<D, 8>(a, w, T, st);
-    }
+    hipLaunchKernelGGL((bwd_reduce<D>), dim3(kSplitSlots / 2, kKvTile / 32), dim3(256), 0, st, w.ctrl,
+                       w.split_tiles, w.partial, a.N, a.Hkv, (__bf16*)a.dk, (__bf16*)a.dv);
+    return hipGetLastError();
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
