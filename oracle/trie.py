@@ -12,6 +12,23 @@ each partition.  Two refinements from the same section:
   branch's first own token [ART "The tree"; DAG "The walk": the last common
   node is copied once per child].
 
+Trainable mode (``trainable`` given, one flag per token): [ART "The tree"]
+keeps trainable tokens out of sharing, and gives each branch a duplicated
+context token at its join point so that the branch's first own token has
+its own prediction position.  Read literally:
+
+* a shared run stops at the first position where any active sequence holds
+  a trainable token (so trainable tokens are never shared, not even between
+  identical sequences);
+* at a fork, a branch whose next token is trainable gets its own copy of
+  the join token; a branch whose next token is not trainable, and a
+  sequence that ends at the fork, hang off the shared token itself;
+* a sequence whose next token is trainable forms a branch of its own even
+  when another sequence has the same token there.
+This is the accounting of the pages' packing example ([ART "Does it
+actually help?"]): a 4,096-token system prompt shared whole, 11,999 shared
+group-prefix tokens and completion + 1 tokens per rollout.
+
 Readings where the pages are silent (all listed in the design doc):
 * the run length compared with ``min_shared`` is measured before the join
   token is split off (a 64-token run that forks stays shared: 63 shared
@@ -44,10 +61,18 @@ class Trie:
         return int(len(self.parent))
 
 
-def build_trie(sequences, min_shared: int = 64) -> Trie:
+def build_trie(sequences, min_shared: int = 64, trainable=None) -> Trie:
     seqs = [np.asarray(s, dtype=np.int64) for s in sequences]
     if min_shared < 1:
         raise ValueError("min_shared must be >= 1")
+    train = None
+    if trainable is not None:
+        train = [np.asarray(t, dtype=bool) for t in trainable]
+        if len(train) != len(seqs) or any(len(t) != len(s) for t, s in zip(train, seqs)):
+            raise ValueError("trainable flags must match the sequences")
+
+    def is_train(s, t):
+        return train is not None and bool(train[s][t])
     parent: List[int] = []
     token: List[int] = []
     paths = [np.full(len(s), -1, dtype=np.int64) for s in seqs]
@@ -65,7 +90,8 @@ def build_trie(sequences, min_shared: int = 64) -> Trie:
         return len(parent) - 1
 
     def common_run_end(active, start):
-        """Smallest end >= start where the active sequences stop agreeing (or the shortest ends)."""
+        """Smallest end >= start where the active sequences stop agreeing (or the shortest ends,
+        or, in trainable mode, any of them reaches a trainable token)."""
         m = min(len(seqs[s]) for s in active)
         ref = seqs[active[0]][start:m]
         end = m
@@ -73,10 +99,16 @@ def build_trie(sequences, min_shared: int = 64) -> Trie:
             diff = np.nonzero(seqs[s][start:m] != ref)[0]
             if len(diff):
                 end = min(end, start + int(diff[0]))
+        if train is not None:
+            for s in active:
+                tr = np.nonzero(train[s][start:end])[0]
+                if len(tr):
+                    end = min(end, start + int(tr[0]))
         return end
 
     def partitions(active, pos):
-        """Split by the token at ``pos``; ended sequences first, then ascending token, stable."""
+        """Split by the token at ``pos``; ended sequences first, then ascending token, stable.
+        In trainable mode a sequence whose token at ``pos`` is trainable is a branch of its own."""
         ended = [s for s in active if len(seqs[s]) == pos]
         going = [s for s in active if len(seqs[s]) > pos]
         going.sort(key=lambda s: int(seqs[s][pos]))          # stable sort keeps input order
@@ -86,7 +118,10 @@ def build_trie(sequences, min_shared: int = 64) -> Trie:
             j = i
             while j < len(going) and seqs[going[j]][pos] == seqs[going[i]][pos]:
                 j += 1
-            parts.append(going[i:j])
+            shared = [s for s in going[i:j] if not is_train(s, pos)]
+            if shared:
+                parts.append(shared)
+            parts.extend([s] for s in going[i:j] if is_train(s, pos))
             i = j
         return parts
 
@@ -105,10 +140,26 @@ def build_trie(sequences, min_shared: int = 64) -> Trie:
         if all(len(seqs[s]) == end for s in active):          # identical remainders: no fork
             emit(active, start, end, par)
             return
-        if end - start >= min_shared:                         # share the run, copy the join token
+        if end - start >= min_shared and train is None:       # share the run, copy the join token
             node = emit(active, start, end - 1, par)
             for part in partitions(active, end):
                 walk(part, end - 1, node)
+        elif end - start >= min_shared:                       # trainable mode: copy where it is needed
+            parts = partitions(active, end)
+            copy = [len(seqs[p[0]]) > end and is_train(p[0], end) for p in parts]
+            if any(copy):
+                node = emit(active, start, end - 1, par)
+                stay = [s for p, c in zip(parts, copy) if not c for s in p]
+                join = emit(stay, end - 1, end, node) if stay else None
+                for p, c in zip(parts, copy):
+                    if c:
+                        walk(p, end - 1, node)
+                    else:
+                        walk(p, end, join)
+            else:
+                node = emit(active, start, end, par)
+                for p in parts:
+                    walk(p, end, node)
         else:                                                 # too short to share: copy it per branch
             for part in partitions(active, end):
                 walk(part, start, par)
