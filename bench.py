@@ -119,6 +119,65 @@ def cpu_baseline(w, total_flops, target_s):
     }
 
 
+def bench_planner(args):
+    """Host row planner on multi-task batches of 12 .. 768 groups, rows of 131,072 tokens.
+
+    Times tree_build_trie (trainable mode) and tree_place_leaves (global best-fit decreasing, and
+    in order), as [ART "Does it actually help?"] tables the tree walk against the bin-packing pass;
+    the oracle runs beside it on the smallest batch.  Prints one JSON line."""
+    import numpy as np
+
+    import prefix_tree_packed_dfs_amd as lib
+    from synth import curriculum_batch
+
+    import ctypes as C
+
+    row = 131072
+    out = []
+    i32, i64, u8 = C.POINTER(C.c_int32), C.POINTER(C.c_int64), C.POINTER(C.c_uint8)
+    for n_groups in (12, 48, 192, 768):
+        seqs, train, grp = curriculum_batch(n_groups)
+        # flattened CSR inputs, built outside the timed region (argument marshalling only)
+        offsets = np.zeros(len(seqs) + 1, dtype=np.int64)
+        np.cumsum([len(x) for x in seqs], out=offsets[1:])
+        tokens = np.concatenate(seqs)
+        flags = np.concatenate(train).view(np.uint8)
+        total = int(offsets[-1])
+        parent = np.empty(total, dtype=np.int32)
+        seq_last = np.empty(len(seqs), dtype=np.int32)
+        n_nodes = C.c_int64(0)
+        t0 = time.perf_counter()
+        st = lib.lib.tree_build_trie(len(seqs), offsets.ctypes.data_as(i64), tokens.ctypes.data_as(i32),
+                                     flags.ctypes.data_as(u8), 64, parent.ctypes.data_as(i32), total,
+                                     C.byref(n_nodes), seq_last.ctypes.data_as(i32))
+        t1 = time.perf_counter()
+        assert st == 0
+        parent = parent[:n_nodes.value]
+        _, tok_g = lib.tree_place_leaves(parent, seq_last, grp, row, "global")
+        t2 = time.perf_counter()
+        _, tok_i = lib.tree_place_leaves(parent, seq_last, grp, row, "in_order")
+        t3 = time.perf_counter()
+        out.append({"groups": n_groups, "completions": len(seqs), "raw_tokens": int(sum(len(x) for x in seqs)),
+                    "trie_nodes": int(len(parent)), "trie_ms": round((t1 - t0) * 1e3, 2),
+                    "place_global_ms": round((t2 - t1) * 1e3, 2), "rows_global": int(len(tok_g)),
+                    "place_in_order_ms": round((t3 - t2) * 1e3, 2), "rows_in_order": int(len(tok_i))})
+    oracle = None
+    if not args.no_cpu_baseline:
+        from oracle.pack import place_leaves, segments
+        from oracle.trie import build_trie
+        seqs, train, grp = curriculum_batch(12)
+        t0 = time.perf_counter()
+        tr = build_trie(seqs, trainable=train)
+        t1 = time.perf_counter()
+        pl = place_leaves(segments(tr.parent, tr.seq_last), grp, row, "global")
+        t2 = time.perf_counter()
+        oracle = {"groups": 12, "trie_s": round(t1 - t0, 3), "place_global_s": round(t2 - t1, 3),
+                  "rows_global": int(len(pl.bin_tokens)), "kind": "oracle", "threads": 1}
+    print(json.dumps({"metric": "row planner: trie walk + best-fit-decreasing placement", "unit": "ms",
+                      "row_len": row, "data": "synthetic (synth.curriculum_batch)", "sizes": out,
+                      "cpu_baseline": oracle}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,7 +188,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB (for calibrating HBM byte counters)")
+    ap.add_argument("--planner", action="store_true",
+                    help="only time the host row planner (trie walk + leaf placement) on curriculum batches")
     args = ap.parse_args()
+    if args.planner:
+        bench_planner(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)

@@ -8,6 +8,7 @@
  * that method, as a plain C ABI:
  *
  *   tree_build_trie      token sequences -> token-level parent array (host)
+ *   tree_place_leaves    sequences of a trie -> fixed-length rows (host)
  *   tree_pack_layout     parent array -> DFS slots, depth, subtree end, token_index (host)
  *   tree_rope            rotary embedding at depth, in place (device)
  *   tree_attn_fwd        masked attention forward (device)
@@ -79,9 +80,20 @@ const char* tree_last_error(void);
  * numbered in emission order, a depth-first pre-order, so
  * tree_pack_layout() of the result keeps node i in slot i.
  *
+ * Trainable mode (`trainable` not NULL), [ART "The tree"]: trainable tokens
+ * are never shared (a shared run stops at the first trainable token of any
+ * active sequence, and a sequence whose next token is trainable is a branch
+ * of its own), and the join token is copied only into branches whose next
+ * token is trainable, so that first trainable token has its own prediction
+ * position; other branches, and sequences ending at the fork, hang off the
+ * shared join token.  This is the accounting of [ART "Does it actually
+ * help?"]: a system prompt shared whole, then 11,999 shared group-prefix
+ * tokens and completion + 1 tokens per rollout.
+ *
  *   n_seqs       number of sequences (>= 0)
  *   seq_offsets  [n_seqs + 1] CSR offsets into `tokens`, non-decreasing, seq_offsets[0] == 0
  *   tokens       [seq_offsets[n_seqs]] token ids (any int32 values)
+ *   trainable    [seq_offsets[n_seqs]] per token, nonzero = trainable; NULL = default mode
  *   min_shared   minimum shared run length (>= 1; 64 is the pages' default)
  *   parent       out [parent_cap] parent node of each node, -1 for a root; NULL = size query
  *   parent_cap   capacity of `parent` in elements; seq_offsets[n_seqs] always suffices
@@ -90,8 +102,57 @@ const char* tree_last_error(void);
  *                may be NULL
  */
 tree_status tree_build_trie(int32_t n_seqs, const int64_t* seq_offsets, const int32_t* tokens,
-                            int32_t min_shared, int32_t* parent, int64_t parent_cap,
-                            int64_t* n_nodes, int32_t* seq_last);
+                            const uint8_t* trainable, int32_t min_shared, int32_t* parent,
+                            int64_t parent_cap, int64_t* n_nodes, int32_t* seq_last);
+
+/* Row placement modes of tree_place_leaves(). */
+typedef enum tree_place_mode {
+    TREE_PLACE_GLOBAL = 0,    /* best-fit decreasing over every leaf of the batch */
+    TREE_PLACE_IN_ORDER = 1   /* one row at a time, in arrival order */
+} tree_place_mode;
+
+/*
+ * tree_place_leaves - assign the sequences of a packed trie to fixed-length
+ * rows (host, synchronous).
+ *
+ * [ART "Bin packing, with a twist"]: a leaf (one sequence) is the list of
+ * segments on its root-to-leaf path; its cost of joining a row is the length
+ * of the segments that row does not hold yet, so a row holds the union of
+ * its leaves' segments.  TREE_PLACE_GLOBAL is best-fit decreasing over that
+ * cost: groups in decreasing order of their most expensive leaf (a leaf's
+ * standalone cost is its path length; equal groups keep the order of their
+ * first sequence), leaves in input order inside a group, each leaf into the
+ * row left with the least free space (the earliest row on a tie), a new row
+ * when none fits.  TREE_PLACE_IN_ORDER is the packer [ART "Does it actually
+ * help?"] compares against: rows filled one at a time in input order, moving
+ * on for good when the next sequence does not fit.
+ *
+ * A segment is a maximal chain of nodes: a node starts one when it is a root,
+ * when its parent has several children, or when its parent is the last
+ * token of a sequence.  A row's token count is therefore the node count of
+ * the sub-forest its sequences span (what a trie rebuilt for the row alone
+ * would hold).
+ *
+ *   n_nodes      nodes of the trie
+ *   parent       [n_nodes] parent node, -1 for a root; every node after its parent
+ *                (the numbering tree_build_trie() produces), else TREE_ERR_BAD_TREE
+ *   n_seqs       number of sequences
+ *   seq_last     [n_seqs] node of each sequence's last token (-1: empty sequence, cost 0)
+ *   group        [n_seqs] group id of each sequence (any int32); may be NULL in
+ *                TREE_PLACE_IN_ORDER mode
+ *   seq_len      row capacity in tokens (>= 1); a sequence longer than a row is
+ *                TREE_ERR_CAPACITY
+ *   mode         a tree_place_mode
+ *   bin_of_seq   out [n_seqs] row of each sequence
+ *   bin_tokens   out [bins_cap] tokens held by each row
+ *   bins_cap     capacity of bin_tokens; fewer rows than needed is TREE_ERR_CAPACITY
+ *                (n_bins and bin_of_seq are still written)
+ *   n_bins       out: number of rows
+ */
+tree_status tree_place_leaves(int32_t n_nodes, const int32_t* parent, int32_t n_seqs,
+                              const int32_t* seq_last, const int32_t* group, int32_t seq_len,
+                              int32_t mode, int32_t* bin_of_seq, int32_t* bin_tokens,
+                              int32_t bins_cap, int32_t* n_bins);
 
 /*
  * tree_pack_layout - lay one packed row out depth-first (host, synchronous).

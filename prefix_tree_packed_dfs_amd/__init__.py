@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     tree_attn_fwd,
     tree_attn_workspace_bytes,
     tree_build_trie,
+    tree_place_leaves,
     tree_pack_layout,
     tree_rope,
     tree_validate_subtree_end,

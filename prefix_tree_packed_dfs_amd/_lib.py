@@ -51,7 +51,11 @@ lib.tree_status_string.restype = C.c_char_p
 lib.tree_status_string.argtypes = [C.c_int]
 lib.tree_last_error.restype = C.c_char_p
 lib.tree_build_trie.restype = C.c_int
-lib.tree_build_trie.argtypes = [C.c_int32, _i64p, _i32p, C.c_int32, _i32p, C.c_int64, _i64p, _i32p]
+lib.tree_build_trie.argtypes = [C.c_int32, _i64p, _i32p, C.POINTER(C.c_uint8), C.c_int32, _i32p, C.c_int64,
+                                _i64p, _i32p]
+lib.tree_place_leaves.restype = C.c_int
+lib.tree_place_leaves.argtypes = [C.c_int32, _i32p, C.c_int32, _i32p, _i32p, C.c_int32, C.c_int32, _i32p,
+                                  _i32p, C.c_int32, _i32p]
 lib.tree_pack_layout.restype = C.c_int
 lib.tree_pack_layout.argtypes = [C.c_int32, _i32p, C.c_int32, _i32p, C.c_int32, _i32p, _i32p, _i32p, _i64p,
                                  _i32p, C.c_int64]
@@ -70,7 +74,7 @@ lib.tree_attn_bwd.argtypes = [C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_in
                               C.c_int64, C.c_int64, C.c_float, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
 
 EXPORTED = ("tree_abi_version", "tree_status_string", "tree_last_error", "tree_build_trie",
-            "tree_pack_layout", "tree_validate_subtree_end", "tree_rope", "tree_attn_workspace_bytes",
+            "tree_place_leaves", "tree_pack_layout", "tree_validate_subtree_end", "tree_rope", "tree_attn_workspace_bytes",
             "tree_attn_fwd", "tree_attn_bwd")
 
 
@@ -89,20 +93,50 @@ def _ptr(a: np.ndarray, ctype):
 # host entry points
 # ---------------------------------------------------------------------------
 
-def tree_build_trie(sequences, min_shared: int = 64):
-    """Token sequences -> (parent int32 [n_nodes], seq_last int32 [n_seqs])."""
+def tree_build_trie(sequences, min_shared: int = 64, trainable=None):
+    """Token sequences -> (parent int32 [n_nodes], seq_last int32 [n_seqs]).
+
+    ``trainable``: optional per-sequence boolean flags per token (trainable mode)."""
     seqs = [np.ascontiguousarray(s, dtype=np.int32) for s in sequences]
     lens = np.asarray([len(s) for s in seqs], dtype=np.int64)
     offsets = np.zeros(len(seqs) + 1, dtype=np.int64)
     np.cumsum(lens, out=offsets[1:])
     tokens = np.concatenate(seqs) if seqs and offsets[-1] > 0 else np.zeros(1, dtype=np.int32)
     total = int(offsets[-1])
+    train = None
+    if trainable is not None:
+        if len(trainable) != len(seqs) or any(len(t) != len(s) for t, s in zip(trainable, seqs)):
+            raise ValueError("trainable flags must match the sequences")
+        flat = [np.asarray(t, dtype=np.uint8) for t in trainable]
+        train = np.concatenate(flat) if total > 0 else np.zeros(1, dtype=np.uint8)
     parent = np.empty(max(total, 1), dtype=np.int32)
     seq_last = np.empty(max(len(seqs), 1), dtype=np.int32)
     n_nodes = C.c_int64(0)
-    _check(lib.tree_build_trie(len(seqs), _ptr(offsets, C.c_int64), _ptr(tokens, C.c_int32), int(min_shared),
+    _check(lib.tree_build_trie(len(seqs), _ptr(offsets, C.c_int64), _ptr(tokens, C.c_int32),
+                               None if train is None else _ptr(train, C.c_uint8), int(min_shared),
                                _ptr(parent, C.c_int32), total, C.byref(n_nodes), _ptr(seq_last, C.c_int32)))
     return parent[:n_nodes.value].copy(), seq_last[:len(seqs)].copy()
+
+
+PLACE_MODES = {"global": 0, "in_order": 1}
+
+
+def tree_place_leaves(parent, seq_last, group, seq_len: int, mode: str = "global"):
+    """Sequences of a trie -> (row of each sequence int32 [n_seqs], tokens per row int32 [n_rows])."""
+    parent = np.ascontiguousarray(parent, dtype=np.int32)
+    seq_last = np.ascontiguousarray(seq_last, dtype=np.int32)
+    n = len(seq_last)
+    grp = None if group is None else np.ascontiguousarray(group, dtype=np.int32)
+    if grp is not None and len(grp) != n:
+        raise ValueError("one group id per sequence")
+    bin_of = np.empty(max(n, 1), dtype=np.int32)
+    cap = max(n, 1)
+    tokens = np.empty(cap, dtype=np.int32)
+    n_bins = C.c_int32(0)
+    _check(lib.tree_place_leaves(len(parent), _ptr(parent, C.c_int32), n, _ptr(seq_last, C.c_int32),
+                                 None if grp is None else _ptr(grp, C.c_int32), int(seq_len), PLACE_MODES[mode],
+                                 _ptr(bin_of, C.c_int32), _ptr(tokens, C.c_int32), cap, C.byref(n_bins)))
+    return bin_of[:n].copy(), tokens[:n_bins.value].copy()
 
 
 @dataclass

@@ -31,7 +31,7 @@ void clear_error() { g_last_error[0] = '\0'; }
 
 using treeattn::fail;
 
-extern "C" int tree_abi_version(void) { return 1; }
+extern "C" int tree_abi_version(void) { return 2; }
 
 extern "C" const char* tree_status_string(int s) {
     switch (s) {
@@ -61,12 +61,14 @@ namespace {
 struct TrieBuilder {
     const int64_t* off;
     const int32_t* tok;
+    const uint8_t* train;  // per token, nonzero = trainable; NULL = no trainable tokens (default mode)
     int32_t min_shared;
     std::vector<int32_t> parent;
     std::vector<int32_t> seq_last;
 
     int64_t len(int32_t s) const { return off[s + 1] - off[s]; }
     int32_t at(int32_t s, int64_t t) const { return tok[off[s] + t]; }
+    bool trained(int32_t s, int64_t t) const { return train && train[off[s] + t]; }
 
     // One node per position in [start, end), shared by every sequence in `act`.
     int32_t emit(const std::vector<int32_t>& act, int64_t start, int64_t end, int32_t par) {
@@ -83,7 +85,9 @@ struct TrieBuilder {
     }
 
     // Split by the token at `pos`: sequences that end at `pos` first, then
-    // ascending token, keeping input order inside a branch.
+    // ascending token, keeping input order inside a branch.  A sequence whose
+    // token at `pos` is trainable is a branch of its own, after the shared
+    // branch of the same token.
     void split(std::vector<int32_t>& act, int64_t pos, std::vector<std::vector<int32_t>>& parts) const {
         std::stable_sort(act.begin(), act.end(), [&](int32_t a, int32_t b) {
             bool ea = len(a) == pos, eb = len(b) == pos;
@@ -102,7 +106,16 @@ struct TrieBuilder {
                 if (!ended && at(act[j], pos) != at(act[i], pos)) break;
                 ++j;
             }
-            parts.emplace_back(act.begin() + i, act.begin() + j);
+            if (ended || !train) {
+                parts.emplace_back(act.begin() + i, act.begin() + j);
+            } else {
+                std::vector<int32_t> shared;
+                for (size_t x = i; x < j; ++x)
+                    if (!trained(act[x], pos)) shared.push_back(act[x]);
+                if (!shared.empty()) parts.push_back(std::move(shared));
+                for (size_t x = i; x < j; ++x)
+                    if (trained(act[x], pos)) parts.push_back({act[x]});
+            }
             i = j;
         }
     }
@@ -137,11 +150,11 @@ struct TrieBuilder {
             }
             int64_t m = len(act[0]);
             for (int32_t s : act) m = std::min(m, len(s));
-            int64_t end = start;
+            int64_t end = start;  // the shared run: equal tokens, none of them trainable
             while (end < m) {
                 int32_t t0 = at(act[0], end);
-                bool same = true;
-                for (size_t i = 1; i < act.size() && same; ++i) same = at(act[i], end) == t0;
+                bool same = !trained(act[0], end);
+                for (size_t i = 1; i < act.size() && same; ++i) same = at(act[i], end) == t0 && !trained(act[i], end);
                 if (!same) break;
                 ++end;
             }
@@ -156,10 +169,33 @@ struct TrieBuilder {
                 emit(act, start, end, it.par);
                 continue;
             }
-            if (end - start >= min_shared) {  // share the run minus the join token
+            if (end - start >= min_shared && !train) {  // share the run minus the join token
                 int32_t node = emit(act, start, end - 1, it.par);
                 split(act, end, parts);
                 push_parts(end - 1, node);
+            } else if (end - start >= min_shared) {
+                // trainable mode: branches whose next token is trainable get a
+                // copy of the join token; the others (and sequences ending
+                // here) hang off the shared join token
+                split(act, end, parts);
+                std::vector<char> copy(parts.size());
+                bool any = false;
+                for (size_t p = 0; p < parts.size(); ++p) {
+                    copy[p] = len(parts[p][0]) > end && trained(parts[p][0], end);
+                    any = any || copy[p];
+                }
+                if (!any) {
+                    int32_t node = emit(act, start, end, it.par);
+                    push_parts(end, node);
+                    continue;
+                }
+                int32_t node = emit(act, start, end - 1, it.par);
+                std::vector<int32_t> stay;
+                for (size_t p = 0; p < parts.size(); ++p)
+                    if (!copy[p]) stay.insert(stay.end(), parts[p].begin(), parts[p].end());
+                const int32_t join = stay.empty() ? -1 : emit(stay, end - 1, end, node);
+                for (size_t p = parts.size(); p-- > 0;)
+                    stack.push_back({std::move(parts[p]), copy[p] ? end - 1 : end, copy[p] ? node : join});
             } else {  // too short: copy it into every branch
                 split(act, end, parts);
                 push_parts(start, it.par);
@@ -171,8 +207,9 @@ struct TrieBuilder {
 }  // namespace
 
 extern "C" tree_status tree_build_trie(int32_t n_seqs, const int64_t* seq_offsets,
-                                       const int32_t* tokens, int32_t min_shared, int32_t* parent,
-                                       int64_t parent_cap, int64_t* n_nodes, int32_t* seq_last) {
+                                       const int32_t* tokens, const uint8_t* trainable, int32_t min_shared,
+                                       int32_t* parent, int64_t parent_cap, int64_t* n_nodes,
+                                       int32_t* seq_last) {
     treeattn::clear_error();
     if (n_seqs < 0) return fail(TREE_ERR_INVALID_ARG, "n_seqs = %d < 0", n_seqs);
     if (!n_nodes) return fail(TREE_ERR_INVALID_ARG, "n_nodes is NULL");
@@ -187,7 +224,7 @@ extern "C" tree_status tree_build_trie(int32_t n_seqs, const int64_t* seq_offset
     if (total > INT32_MAX) return fail(TREE_ERR_UNSUPPORTED, "more than 2^31-1 tokens");
     if (parent && parent_cap < 0) return fail(TREE_ERR_INVALID_ARG, "parent_cap < 0");
 
-    TrieBuilder tb{seq_offsets, tokens, min_shared, {}, {}};
+    TrieBuilder tb{seq_offsets, tokens, trainable, min_shared, {}, {}};
     tb.parent.reserve((size_t)total);
     tb.seq_last.assign((size_t)n_seqs, -1);
     if (n_seqs > 0) tb.run(n_seqs);
@@ -305,5 +342,163 @@ extern "C" tree_status tree_validate_subtree_end(const int32_t* se, int64_t n) {
                         (long long)j);
         open.push_back(se[j]);
     }
+    return TREE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// tree_place_leaves
+// ---------------------------------------------------------------------------
+
+extern "C" tree_status tree_place_leaves(int32_t n_nodes, const int32_t* parent, int32_t n_seqs,
+                                         const int32_t* seq_last, const int32_t* group, int32_t seq_len,
+                                         int32_t mode, int32_t* bin_of_seq, int32_t* bin_tokens,
+                                         int32_t bins_cap, int32_t* n_bins) {
+    treeattn::clear_error();
+    if (n_nodes < 0 || n_seqs < 0) return fail(TREE_ERR_INVALID_ARG, "negative size");
+    if (seq_len < 1) return fail(TREE_ERR_INVALID_ARG, "seq_len = %d < 1", seq_len);
+    if (mode != TREE_PLACE_GLOBAL && mode != TREE_PLACE_IN_ORDER)
+        return fail(TREE_ERR_INVALID_ARG, "unknown placement mode %d", mode);
+    if (!n_bins || (n_nodes > 0 && !parent) || (n_seqs > 0 && (!seq_last || !bin_of_seq)) ||
+        (mode == TREE_PLACE_GLOBAL && n_seqs > 0 && !group) || (bins_cap > 0 && !bin_tokens))
+        return fail(TREE_ERR_INVALID_ARG, "null pointer argument");
+    for (int32_t v = 0; v < n_nodes; ++v)
+        if (parent[v] < -1 || parent[v] >= v)
+            return fail(TREE_ERR_BAD_TREE, "parent[%d] = %d: nodes must follow their parent", v, parent[v]);
+    for (int32_t s = 0; s < n_seqs; ++s)
+        if (seq_last[s] < -1 || seq_last[s] >= n_nodes)
+            return fail(TREE_ERR_BAD_TREE, "seq_last[%d] = %d out of range", s, seq_last[s]);
+
+    // segments: maximal chains; a node starts one at a root, below a fork, or
+    // below the last token of a sequence [ART "Bin packing, with a twist"]
+    // per node: bit 0-1 child count saturated at 2, bit 2 = last token of a sequence
+    std::vector<uint8_t> flag((size_t)n_nodes, 0);
+    std::vector<int32_t> seg_of((size_t)n_nodes);
+    for (int32_t v = 0; v < n_nodes; ++v)
+        if (parent[v] >= 0 && (flag[parent[v]] & 3) < 2) ++flag[parent[v]];
+    for (int32_t s = 0; s < n_seqs; ++s)
+        if (seq_last[s] >= 0) flag[seq_last[s]] |= 4;
+    std::vector<int64_t> seg_len;
+    std::vector<int32_t> seg_up;  // segment of the parent of the segment's first node, -1 at a root
+    for (int32_t v = 0; v < n_nodes; ++v) {
+        const int32_t p = parent[v];
+        if (p < 0 || (flag[p] & 3) > 1 || (flag[p] & 4)) {
+            seg_of[v] = (int32_t)seg_len.size();
+            seg_len.push_back(0);
+            seg_up.push_back(p < 0 ? -1 : seg_of[p]);
+        } else {
+            seg_of[v] = seg_of[p];
+        }
+        ++seg_len[seg_of[v]];
+    }
+    // each sequence's segments (root first) and standalone cost
+    std::vector<int64_t> poff((size_t)n_seqs + 1, 0), cost((size_t)n_seqs, 0);
+    std::vector<int32_t> path;
+    for (int32_t s = 0; s < n_seqs; ++s) {
+        int32_t d = 0;
+        for (int32_t x = seq_last[s] < 0 ? -1 : seg_of[seq_last[s]]; x >= 0; x = seg_up[x]) ++d;
+        poff[s + 1] = poff[s] + d;
+    }
+    path.resize((size_t)poff[n_seqs]);
+    for (int32_t s = 0; s < n_seqs; ++s) {
+        int64_t p = poff[s + 1];
+        for (int32_t x = seq_last[s] < 0 ? -1 : seg_of[seq_last[s]]; x >= 0; x = seg_up[x]) {
+            path[--p] = x;
+            cost[s] += seg_len[x];
+        }
+        if (cost[s] > seq_len)
+            return fail(TREE_ERR_CAPACITY, "sequence %d needs %lld tokens, more than a row of %d", s,
+                        (long long)cost[s], seq_len);
+    }
+
+    // rows: tokens held, and for each segment the rows that hold it
+    std::vector<int64_t> tokens;
+    std::vector<std::vector<int32_t>> rows_of(seg_len.size());
+    std::vector<int64_t> shared;  // per row: tokens of the current leaf it already holds
+    std::vector<int32_t> touched;
+    auto gather = [&](int32_t s) {  // shared[b] for every row b touching leaf s
+        for (int32_t b : touched) shared[b] = 0;
+        touched.clear();
+        for (int64_t i = poff[s]; i < poff[s + 1]; ++i)
+            for (int32_t b : rows_of[path[i]]) {
+                if (shared[b] == 0) touched.push_back(b);
+                shared[b] += seg_len[path[i]];
+            }
+    };
+    auto add = [&](int32_t b, int32_t s) {
+        tokens[b] += cost[s] - shared[b];
+        for (int64_t i = poff[s]; i < poff[s + 1]; ++i) {
+            std::vector<int32_t>& r = rows_of[path[i]];
+            if (r.empty() || r.back() != b) {
+                if (std::find(r.begin(), r.end(), b) == r.end()) r.push_back(b);
+            }
+        }
+        bin_of_seq[s] = b;
+    };
+    auto new_row = [&]() {
+        tokens.push_back(0);
+        shared.push_back(0);
+        return (int32_t)tokens.size() - 1;
+    };
+
+    if (mode == TREE_PLACE_IN_ORDER) {
+        // [ART "Does it actually help?"]: fill one row at a time in arrival
+        // order, moving on for good when the next sequence does not fit
+        int32_t cur = -1;
+        for (int32_t s = 0; s < n_seqs; ++s) {
+            gather(s);
+            if (cur < 0 || tokens[cur] + cost[s] - shared[cur] > seq_len) {
+                cur = new_row();
+                gather(s);
+            }
+            add(cur, s);
+        }
+    } else {
+        // [ART "Bin packing, with a twist"]: groups in decreasing order of their
+        // most expensive leaf (stable), leaves in input order; each leaf into
+        // the row left with the least free space, a new row if none fits
+        std::vector<int32_t> gid;                // distinct group ids, first-appearance order
+        std::vector<std::vector<int32_t>> members;
+        {
+            std::vector<std::pair<int32_t, int32_t>> key((size_t)n_seqs);
+            for (int32_t s = 0; s < n_seqs; ++s) key[s] = {group[s], s};
+            std::stable_sort(key.begin(), key.end());
+            std::vector<std::pair<int32_t, int32_t>> first;  // (first sequence, group index)
+            for (size_t i = 0; i < key.size();) {
+                size_t j = i;
+                members.emplace_back();
+                while (j < key.size() && key[j].first == key[i].first) members.back().push_back(key[j++].second);
+                first.push_back({members.back()[0], (int32_t)members.size() - 1});
+                i = j;
+            }
+            std::sort(first.begin(), first.end());
+            for (auto& f : first) gid.push_back(f.second);
+        }
+        std::vector<int64_t> gmax(members.size(), 0);
+        for (size_t g = 0; g < members.size(); ++g)
+            for (int32_t s : members[g]) gmax[g] = std::max(gmax[g], cost[s]);
+        std::stable_sort(gid.begin(), gid.end(), [&](int32_t a, int32_t b) { return gmax[a] > gmax[b]; });
+        for (int32_t g : gid)
+            for (int32_t s : members[g]) {
+                gather(s);
+                int32_t best = -1;
+                int64_t best_free = (int64_t)seq_len + 1;
+                for (int32_t b = 0; b < (int32_t)tokens.size(); ++b) {
+                    const int64_t c = tokens[b] + cost[s] - shared[b];
+                    if (c <= seq_len && seq_len - c < best_free) {
+                        best = b;
+                        best_free = seq_len - c;
+                    }
+                }
+                if (best < 0) {
+                    best = new_row();
+                    gather(s);
+                }
+                add(best, s);
+            }
+    }
+    *n_bins = (int32_t)tokens.size();
+    if ((int64_t)tokens.size() > bins_cap)
+        return fail(TREE_ERR_CAPACITY, "bins_cap %d < %zu rows", bins_cap, tokens.size());
+    for (size_t b = 0; b < tokens.size(); ++b) bin_tokens[b] = (int32_t)tokens[b];
     return TREE_OK;
 }

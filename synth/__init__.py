@@ -11,4 +11,5 @@ from .workloads import (  # noqa: F401
     round_bf16,
     feature_tables,
     from_sequences,
+    curriculum_batch,
 )

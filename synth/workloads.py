@@ -323,3 +323,33 @@ def feature_tables(w: Workload, which=("q", "k", "v", "do")) -> dict:
             x = round_bf16(x)
         out[name] = x
     return out
+
+
+def curriculum_batch(n_groups: int, seed: int = 6000, n_system: int = 4, system_len: int = 4096,
+                     prefix_lo: int = 2000, prefix_hi: int = 16000, group_lo: int = 4, group_hi: int = 13,
+                     comp_lo: int = 4000, comp_hi: int = 28000):
+    """A multi-task batch for the row planner: ``n_groups`` RL groups, each a task prefix under one
+    of ``n_system`` shared system prompts, with U{group_lo..group_hi} trainable completions.
+
+    Returns (sequences, trainable flags, group id per sequence).  Token ids are fresh random
+    values, so sharing comes only from the stated structure.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    systems = [rng.integers(0, TOKEN_HIGH, size=system_len, dtype=np.int64).astype(np.int32)
+               for _ in range(n_system)]
+    for i, s in enumerate(systems):
+        s[0] = i            # distinct first tokens: the system prompts do not share a prefix
+    seqs, train, group = [], [], []
+    for g in range(n_groups):
+        sysp = systems[int(rng.integers(0, n_system))]
+        prefix = rng.integers(0, TOKEN_HIGH, size=int(rng.integers(prefix_lo, prefix_hi + 1)),
+                              dtype=np.int64).astype(np.int32)
+        for _ in range(int(rng.integers(group_lo, group_hi + 1))):
+            comp = rng.integers(0, TOKEN_HIGH, size=int(rng.integers(comp_lo, comp_hi + 1)),
+                                dtype=np.int64).astype(np.int32)
+            seqs.append(np.concatenate([sysp, prefix, comp]))
+            t = np.zeros(len(seqs[-1]), dtype=bool)
+            t[len(sysp) + len(prefix):] = True
+            train.append(t)
+            group.append(g)
+    return seqs, train, np.asarray(group, dtype=np.int32)

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert declared == set(lib.EXPORTED)
     for name in declared:
         assert hasattr(lib.lib, name), name
-    assert lib.lib.tree_abi_version() == 1
+    assert lib.lib.tree_abi_version() == 2
 
 
 def _random_sequences(rng, n, max_len, vocab):
@@ -130,11 +130,11 @@ def test_capacity_and_size_query():
     toks = np.array([1, 2, 3, 1, 2, 4], dtype=np.int32)
     n = C.c_int64(0)
     i32 = C.POINTER(C.c_int32)
-    st = L.tree_build_trie(2, offs.ctypes.data_as(C.POINTER(C.c_int64)), toks.ctypes.data_as(i32), 1, None, 0,
-                           C.byref(n), None)
+    st = L.tree_build_trie(2, offs.ctypes.data_as(C.POINTER(C.c_int64)), toks.ctypes.data_as(i32), None, 1, None,
+                           0, C.byref(n), None)
     assert st == 0 and n.value == 1 + 2 * 2
     small = np.zeros(2, np.int32)
-    st = L.tree_build_trie(2, offs.ctypes.data_as(C.POINTER(C.c_int64)), toks.ctypes.data_as(i32), 1,
+    st = L.tree_build_trie(2, offs.ctypes.data_as(C.POINTER(C.c_int64)), toks.ctypes.data_as(i32), None, 1,
                            small.ctypes.data_as(i32), 2, C.byref(n), None)
     assert st == 3 and n.value == 5
     parent = np.array([-1, 0, 0], np.int32)
