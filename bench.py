@@ -178,6 +178,127 @@ def bench_planner(args):
                       "cpu_baseline": oracle}), flush=True)
 
 
+def bench_sweep(args):
+    """Tree packing against sequence packing over packing ratios 1.0 .. 4.9, same kernels.
+
+    Sequence packing lays each sequence out as its own chain (a forest of chains: plain
+    varlen causal attention); tree packing lays out the trie.  Each layout gets the same
+    per-token q/k/v/dout (gathered from one set of tree-slot tensors) and runs rope(q),
+    rope(k), tree_attn_fwd, tree_attn_bwd on device; layouts are on the host beforehand.
+    Each layout is timed twice, alternating with the other, and reports its faster run.
+    Peak memory is the device memory the layout's step allocates: its q/k/v/dout,
+    out/lse, dq/dk/dv and workspaces.  [TRL tree packing, "Claimed vs. verified"] reports
+    the same comparison (speedup and peak memory against packing ratio) for FlashAttention 3
+    on another GPU.  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import prefix_tree_packed_dfs_amd as lib
+    from synth import grpo_group, agentic_trie, independent, long_history, sequence_packing_forest, shared_history
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    points = [shared_history(p) for p in (0, 1000, 2000, 4000, 8000, 20000)]
+    points += [independent(), grpo_group(), agentic_trie(), long_history()]
+    steps, warmup = args.steps, args.warmup
+
+    def pad64(n):
+        return max(64, (n + 63) // 64 * 64)
+
+    def layout(w, parent, seq_last):
+        R = pad64(len(parent))
+        lay = lib.tree_pack_layout(parent, seq_last, R)
+        ti = np.concatenate([lay.sequence_slots(s) for s in range(len(w.sequences))]).astype(np.int64)
+        pairs = int((lay.pos_ids[:len(parent)].astype(np.int64) + 1).sum())
+        return lay, R, ti, pairs, len(parent)
+
+    def run(w, lay, R, src, gather, pairs):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        q, k, v, do = (t[:, gather].contiguous() for t in src)
+        pos = torch.from_numpy(lay.pos_ids.astype(np.int32)).view(1, R).to(dev)
+        se = torch.from_numpy(lay.subtree_end.astype(np.int32)).view(1, R).to(dev)
+        dt = lib.TREE_BF16
+        out = torch.empty_like(q)
+        lse = torch.empty((1, w.Hq, R), device=dev, dtype=torch.float32)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        wsf = torch.empty(max(lib.tree_attn_workspace_bytes(dt, 1, R, w.Hq, w.Hkv, w.D, False), 1), device=dev,
+                          dtype=torch.uint8)
+        wsb = torch.empty(max(lib.tree_attn_workspace_bytes(dt, 1, R, w.Hq, w.Hkv, w.D, True), 1), device=dev,
+                          dtype=torch.uint8)
+        scale = w.D ** -0.5
+
+        def step(ev=None):
+            if ev:
+                ev[0].record()
+            lib.tree_rope(q, pos, w.theta)
+            lib.tree_rope(k, pos, w.theta)
+            lib.tree_attn_fwd(q, k, v, se, scale, out=out, lse=lse, ws=wsf)
+            if ev:
+                ev[1].record()
+            lib.tree_attn_bwd(q, k, v, se, out, lse, do, scale, dq=dq, dk=dk, dv=dv, ws=wsb)
+            if ev:
+                ev[2].record()
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
+        fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        del q, k, v, do, out, lse, dq, dk, dv, wsf, wsb, pos, se
+        flops = 3.5 * 4.0 * w.D * w.Hq * pairs
+        return {"row_len": R, "ancestor_pairs_per_head": pairs, "ms_per_step": round(ms, 4),
+                "rope_fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4), "peak_bytes": int(peak),
+                "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                "raw_tok_s": round(w.raw_tokens / (ms * 1e-3), 1)}
+
+    rows = []
+    for w in points:
+        print(f"# {w.name}: {len(w.sequences)} sequences, {w.raw_tokens} raw tokens", file=sys.stderr, flush=True)
+        tlay, tR, tti, tpairs, n = layout(w, *lib.tree_build_trie(w.sequences, min_shared=64))
+        clay, cR, cti, cpairs, _ = layout(w, *sequence_packing_forest(w.sequences))
+        g = torch.Generator(device=dev).manual_seed(7)
+        src = [torch.randn((1, tR, h, w.D), generator=g, device=dev).to(torch.bfloat16)
+               for h in (w.Hq, w.Hkv, w.Hkv, w.Hq)]
+        # chain slot c holds the token whose tree slot is gather[c]; padding slots read tree slot 0
+        gather = np.zeros(cR, np.int64)
+        gather[cti] = tti
+        tidx, cidx = torch.arange(tR, device=dev), torch.from_numpy(gather).to(dev)
+        if not rows:  # bring the clocks up before the first timed run
+            run(w, tlay, tR, src, tidx, tpairs)
+        # two alternating runs per layout; each layout reports its faster run
+        t_runs, c_runs = [], []
+        for _ in range(2):
+            t_runs.append(run(w, tlay, tR, src, tidx, tpairs))
+            c_runs.append(run(w, clay, cR, src, cidx, cpairs))
+        tree = min(t_runs, key=lambda r: r["ms_per_step"])
+        seqp = min(c_runs, key=lambda r: r["ms_per_step"])
+        del src
+        rows.append({
+            "workload": w.name, "sequences": len(w.sequences), "raw_tokens": w.raw_tokens,
+            "forwarded_tokens": n, "packing_ratio": round(w.raw_tokens / n, 4),
+            "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
+            "tree": tree, "sequence_packing": seqp,
+            "speedup": round(seqp["ms_per_step"] / tree["ms_per_step"], 3),
+            "memory_ratio": round(seqp["peak_bytes"] / tree["peak_bytes"], 3),
+            "pair_ratio": round(cpairs / tpairs, 3),
+        })
+        print(f"#   ratio {rows[-1]['packing_ratio']}: tree {tree['ms_per_step']} ms, sequence packing "
+              f"{seqp['ms_per_step']} ms, speedup {rows[-1]['speedup']}, memory "
+              f"{seqp['peak_bytes'] / 2**30:.2f} -> {tree['peak_bytes'] / 2**30:.2f} GiB", file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "tree packing vs sequence packing: fwd+bwd attention step time and peak memory",
+                      "unit": "x (sequence-packing time / tree time)", "steps": steps, "warmup": warmup,
+                      "dtype": "bf16", "data": "synthetic", "points": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,7 +311,15 @@ def main():
                     help="only run a plain device copy of 1 GiB (for calibrating HBM byte counters)")
     ap.add_argument("--planner", action="store_true",
                     help="only time the host row planner (trie walk + leaf placement) on curriculum batches")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the tree-vs-sequence-packing sweep over packing ratios 1.0 .. 4.9")
     args = ap.parse_args()
+    if args.sweep:
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_sweep(args)
+        return
     if args.planner:
         bench_planner(args)
         return

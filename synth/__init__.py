@@ -12,4 +12,6 @@ from .workloads import (  # noqa: F401
     feature_tables,
     from_sequences,
     curriculum_batch,
+    shared_history,
+    sequence_packing_forest,
 )

@@ -261,6 +261,42 @@ def long_history(seed_base: int = 5000, prefix: int = 20000, n: int = 8, unique:
     return _finish("long_history", tree, Hq, Hkv, D, dtype, row_len, seed_base)
 
 
+def shared_history(prefix: int, n: int = 8, unique: int = 2000, seed_base: int = 7000, Hq: int = 16,
+                   Hkv: int = 8, D: int = 128, dtype: str = "bf16") -> Workload:
+    """``n`` rollouts of ``unique`` tokens after a shared history of ``prefix`` tokens (none if 0).
+
+    The packing ratio is n (prefix + unique) / (prefix + n unique), plus the join copies; rows
+    are padded to a multiple of 64.  prefix 20000, n 8, unique 2000 is the agent-history
+    example of [explainx.ai on TRL tree packing, "A back-of-envelope example"] (ratio 4.9).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed_base + prefix))
+    tree = _SegmentTree(rng)
+    if prefix > 0:
+        root = tree.add(-1, prefix)
+        tree.add_children(root, [unique] * n)
+    else:
+        for f in tree.first_tokens(n).tolist():
+            tree.add(-1, unique, f)
+    return _finish(f"shared_history_p{prefix}", tree, Hq, Hkv, D, dtype, None, seed_base + prefix)
+
+
+def sequence_packing_forest(sequences):
+    """Parent array and last node of every sequence when nothing is shared: one chain per sequence.
+
+    Node ids run through the sequences in order (sequence s holds ids o_s .. o_s + len_s - 1, its
+    first token a root, each later token the child of the one before).  Laid out depth first,
+    this is plain sequence packing: each token attends to the tokens before it in its own
+    sequence and positions restart at 0 in every sequence.
+    """
+    lens = np.array([len(s) for s in sequences], dtype=np.int64)
+    total = int(lens.sum())
+    parent = np.arange(-1, total - 1, dtype=np.int64)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]) if len(lens) else np.zeros(0, np.int64)
+    parent[starts[lens > 0]] = -1
+    seq_last = np.where(lens > 0, starts + lens - 1, -1)
+    return parent.astype(np.int32), seq_last.astype(np.int32)
+
+
 def from_sequences(sequences, *, Hq: int, Hkv: int, D: int, dtype: str, seed_base: int,
                    row_len: Optional[int] = None, backward: bool = True, theta: float = 10000.0,
                    name: str = "custom") -> Workload:

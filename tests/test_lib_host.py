@@ -162,3 +162,26 @@ def test_device_entry_points_reject_bad_arguments_before_any_launch():
     assert L.tree_attn_workspace_bytes(1, 1, 8, 4, 2, 96, 1) == 0
     # empty batches are a no-op
     assert L.tree_attn_fwd(1, None, None, None, None, 0, 8, 4, 2, 64, 1.0, None, None, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_sequence_packing_forest_is_plain_varlen_causal(seed):
+    """One chain per sequence: positions restart at 0, every token's interval ends at its sequence's end."""
+    from synth import sequence_packing_forest
+    rng = np.random.default_rng(500 + seed)
+    seqs = _random_sequences(rng, int(rng.integers(1, 10)), 40, 3)
+    parent, seq_last = sequence_packing_forest(seqs)
+    lens = np.array([len(s) for s in seqs])
+    total = int(lens.sum())
+    R = total + int(rng.integers(0, 5))
+    lay = lib.tree_pack_layout(parent, seq_last, R)
+    ends = np.cumsum(lens)
+    starts = ends - lens
+    for s in range(len(seqs)):
+        sl = lay.sequence_slots(s)
+        assert np.array_equal(sl, np.arange(starts[s], ends[s]))
+        assert np.array_equal(lay.pos_ids[sl], np.arange(lens[s]))
+        assert np.all(lay.subtree_end[sl] == ends[s] - 1)
+    assert np.array_equal(lay.subtree_end[total:], np.arange(total, R))
+    rl = dfs_layout(parent, seq_last, R)
+    assert np.array_equal(lay.subtree_end, rl.subtree_end) and np.array_equal(lay.pos_ids, rl.pos_ids)
