@@ -35,12 +35,13 @@ COPY_BYTES = 1 << 30         # size of the plain copy used to calibrate the HBM 
 
 
 def source_hash() -> str:
-    """Hash of the kernel sources: counter-based traffic is only reported for the kernels it was taken on."""
+    """Hash of the attention kernel sources: counter-based traffic is only reported for the kernels it
+    was taken on."""
     import hashlib
     d = os.path.join(ROOT, "prefix_tree_packed_dfs_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".cpp", ".h")):
+        if f.startswith("attn_") or f == "mfma_common.h":
             h.update(f.encode())
             h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]

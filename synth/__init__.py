@@ -14,4 +14,5 @@ from .workloads import (  # noqa: F401
     curriculum_batch,
     shared_history,
     sequence_packing_forest,
+    gdn_tables,
 )

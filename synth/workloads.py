@@ -389,3 +389,23 @@ def curriculum_batch(n_groups: int, seed: int = 6000, n_system: int = 4, system_
             train.append(t)
             group.append(g)
     return seqs, train, np.asarray(group, dtype=np.int32)
+
+
+def gdn_tables(w: Workload, Hk: int = 16, Hv: int = 32, dk: int = 128, dv: int = 128, conv_width: int = 4) -> dict:
+    """Inputs of a gated-delta-rule mixing layer for a workload, per distinct prefix.
+
+    x [n_feat, 2*Hk*dk + Hv*dv] ~ N(0, 1) (channels q | k | v; bf16 workloads round to bf16);
+    conv weights [C, conv_width] ~ N(0, 1/conv_width); log-decay g [n_feat, Hv] = -c_h u with
+    u ~ U(0, 1) and c_h log-spaced over the value heads from 1e-4 (memory of ~10^4 tokens) to 0.5;
+    beta [n_feat, Hv] = sigmoid(N(0, 1)).  g and beta are float32.  Seeds ``seed_base + 11..14``.
+    """
+    C = 2 * Hk * dk + Hv * dv
+    rng = lambda i: np.random.Generator(np.random.PCG64(w.seed_base + i))  # noqa: E731
+    x = rng(11).standard_normal((w.n_feat, C), dtype=np.float32)
+    if w.dtype == "bf16":
+        x = round_bf16(x)
+    conv_w = (rng(12).standard_normal((C, conv_width)) / np.sqrt(conv_width)).astype(np.float32)
+    c = np.exp(np.linspace(np.log(1e-4), np.log(0.5), Hv))
+    g = (-c[None, :] * rng(13).random((w.n_feat, Hv))).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-rng(14).standard_normal((w.n_feat, Hv))))).astype(np.float32)
+    return {"x": x, "conv_w": conv_w, "g": g, "beta": beta}
