@@ -13,6 +13,8 @@
  *   tree_rope            rotary embedding at depth, in place (device)
  *   tree_attn_fwd        masked attention forward (device)
  *   tree_attn_bwd        its exact gradient (device)
+ *   tree_gdn_plan        DFS row -> chains, 64-token chunks, depth buckets (host)
+ *   tree_gdn_fwd         gated-delta-rule mixing over the row (device)
  *
  * Sources (web pages, cited by title and section):
  *   [ART] "Prefix Tree Packing in ART" (FurtherAI blog)
@@ -263,6 +265,88 @@ tree_status tree_attn_bwd(tree_dtype dt, const void* q, const void* k, const voi
                           const void* dout, int64_t B, int64_t N, int64_t Hq, int64_t Hkv,
                           int64_t D, float softmax_scale, void* dq, void* dk, void* dv, void* ws,
                           size_t ws_bytes, void* stream);
+
+/*
+ * Gated-delta-rule (GDN) token mixing over a packed row.
+ *
+ * [ART "Token-mixing layers"]: a recurrent layer has no mask; its state runs
+ * token by token along each root-to-leaf path, is forked at every branch
+ * point and starts from zero at every tree root.  Its pages run it depth by
+ * depth over the tree's segments, a causal convolution and a chunked (64
+ * token) delta-rule call per depth, a child starting from its parent's final
+ * state.  The layer is Gated DeltaNet (Yang, Kautz and Hatamizadeh, 2024):
+ * per slot t, x_t holds C = 2 Hk dk + Hv dv channels, ordered q | k | v; a
+ * depthwise causal convolution of width W over the slot and its W-1 nearest
+ * ancestors (zeros above a root; tap W-1 weighs the slot itself), then SiLU;
+ * q and k divided by their L2 norm per head (zero stays zero), q scaled by
+ * dk^-1/2; then per value head h (key head h / (Hv / Hk)), with state
+ * S in R^{dv x dk}:
+ *     S_t = exp(g_t) S_parent (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,
+ * S_parent the state after the slot's parent (zero for a root).
+ */
+
+/*
+ * tree_gdn_plan - the work plan of tree_gdn_fwd for one packed row (host).
+ *
+ * The parent of each slot is the innermost interval [j, subtree_end[j]]
+ * containing it.  A chain is a maximal run of consecutive slots each of which
+ * is the only child of the one before; every chain starts from one state (zero
+ * at a root, else the final state of the chain ending at its parent).  Chains
+ * are bucketed by depth (the number of chains above them) and cut into chunks
+ * of up to 64 slots from the chain's first slot.  A chunk that ends a chain
+ * short of 64 slots is run as it is (its final state is exact), so no tail is
+ * replayed per child.
+ *
+ *   n              real slots of the row (padding slots after them are not given)
+ *   subtree_end    [n] the row's subtree_end (tree_pack_layout), validated here
+ *   parent_slot    out [n] parent slot, -1 at roots
+ *   segments       out [seg_cap][4] per chain, depth-major: first chunk, chunk count,
+ *                  state slot of the parent chain (-1 at a root: zero state), own
+ *                  state slot (-1 for a chain without children: its final state is
+ *                  not kept); slots number the chains with children in plan order
+ *   chunks         out [chunk_cap][2] per chunk, chain by chain: first slot, length (1..64)
+ *   depth_offsets  out [depth_cap + 1] chains of depth d are segments[depth_offsets[d] ..
+ *                  depth_offsets[d+1])
+ *   n_segments, n_chunks, n_depths, n_states   out: counts (written also on TREE_ERR_CAPACITY)
+ * All four arrays NULL: size query.  TREE_ERR_BAD_TREE for a subtree_end that
+ * is not a nested interval set.
+ */
+tree_status tree_gdn_plan(int64_t n, const int32_t* subtree_end, int32_t* parent_slot, int32_t* segments,
+                          int64_t seg_cap, int64_t* n_segments, int32_t* chunks, int64_t chunk_cap,
+                          int64_t* n_chunks, int32_t* depth_offsets, int64_t depth_cap, int64_t* n_depths,
+                          int64_t* n_states);
+
+/*
+ * tree_gdn_workspace_bytes - device workspace of tree_gdn_fwd (0 for
+ * unsupported sizes).  It holds the convolved inputs ([n, C] bf16), the
+ * chunk operands (57,856 bytes per chunk and value head) and the final state
+ * of every chain with children (fp32 [n_states, Hv, dk, dv]).
+ */
+size_t tree_gdn_workspace_bytes(int64_t n, int64_t n_states, int64_t n_chunks, int64_t Hk, int64_t Hv,
+                                int64_t dk, int64_t dv);
+
+/*
+ * tree_gdn_fwd - gated-delta-rule mixing over one packed row (device, async).
+ *
+ *   dt             TREE_BF16 (x and out bf16; gates fp32; state fp32)
+ *   x              [n, C] mixing input, C = 2 Hk dk + Hv dv, channels q | k | v
+ *   conv_w         [C, conv_width] fp32 convolution taps, conv_width 1..4
+ *   g, beta        [n, Hv] fp32 log decay (<= 0) and write strength per slot and value head
+ *   parent_slot, segments, chunks   device copies of tree_gdn_plan's outputs
+ *   depth_offsets  HOST array [n_depths + 1] from tree_gdn_plan (launch sizes)
+ *   n_states       tree_gdn_plan's state count
+ *   n              real slots; Hk, Hv heads (Hv a multiple of Hk); dk = dv = 128
+ *   out            [n, Hv, dv] bf16
+ *   ws, ws_bytes   device workspace of at least tree_gdn_workspace_bytes() bytes
+ * The device tables are trusted: pass tree_gdn_plan's output for this row.
+ * Work: one convolution launch, one chunk launch, one state launch per depth.
+ */
+tree_status tree_gdn_fwd(tree_dtype dt, const void* x, const float* conv_w, int64_t conv_width, const float* g,
+                         const float* beta, const int32_t* parent_slot, const int32_t* segments,
+                         int64_t n_segments, const int32_t* chunks, int64_t n_chunks, const int32_t* depth_offsets,
+                         int64_t n_depths, int64_t n_states, int64_t n, int64_t Hk, int64_t Hv, int64_t dk,
+                         int64_t dv, void* out, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,4 +1,4 @@
-"""Attention over prefix-tree-packed rows on AMD Instinct MI355X (gfx950).
+"""Attention and gated-delta-rule mixing over prefix-tree-packed rows on AMD Instinct MI355X (gfx950).
 
 The Python names mirror the C entry points of include/tree_attn.h; all work
 happens in libtreeattn.so (host C++ for the integer layout, HIP kernels for
@@ -7,6 +7,7 @@ everything on the device).
 
 from ._lib import (  # noqa: F401
     EXPORTED,
+    GdnPlan,
     TREE_BF16,
     TREE_F32,
     PackedLayout,
@@ -16,6 +17,9 @@ from ._lib import (  # noqa: F401
     tree_attn_fwd,
     tree_attn_workspace_bytes,
     tree_build_trie,
+    tree_gdn_fwd,
+    tree_gdn_plan,
+    tree_gdn_workspace_bytes,
     tree_place_leaves,
     tree_pack_layout,
     tree_rope,

@@ -73,9 +73,19 @@ lib.tree_attn_bwd.restype = C.c_int
 lib.tree_attn_bwd.argtypes = [C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int64, C.c_int64, C.c_int64,
                               C.c_int64, C.c_int64, C.c_float, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
 
+lib.tree_gdn_plan.restype = C.c_int
+lib.tree_gdn_plan.argtypes = [C.c_int64, _i32p, _i32p, _i32p, C.c_int64, _i64p, _i32p, C.c_int64, _i64p, _i32p,
+                              C.c_int64, _i64p, _i64p]
+lib.tree_gdn_workspace_bytes.restype = C.c_size_t
+lib.tree_gdn_workspace_bytes.argtypes = [C.c_int64] * 7
+lib.tree_gdn_fwd.restype = C.c_int
+lib.tree_gdn_fwd.argtypes = [C.c_int, _vp, _vp, C.c_int64, _vp, _vp, _vp, _vp, C.c_int64, _vp, C.c_int64, _i32p,
+                             C.c_int64, C.c_int64, C.c_int64, C.c_int64, C.c_int64, C.c_int64, C.c_int64, _vp, _vp,
+                             C.c_size_t, _vp]
+
 EXPORTED = ("tree_abi_version", "tree_status_string", "tree_last_error", "tree_build_trie",
             "tree_place_leaves", "tree_pack_layout", "tree_validate_subtree_end", "tree_rope", "tree_attn_workspace_bytes",
-            "tree_attn_fwd", "tree_attn_bwd")
+            "tree_attn_fwd", "tree_attn_bwd", "tree_gdn_plan", "tree_gdn_workspace_bytes", "tree_gdn_fwd")
 
 
 def _check(status: int):
@@ -284,3 +294,96 @@ def tree_attn_bwd(q, k, v, subtree_end, out, lse, dout, softmax_scale=None, dq=N
                              _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), ws.data_ptr(),
                              ws.numel() * ws.element_size(), _stream()))
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# gated-delta-rule mixing
+# ---------------------------------------------------------------------------
+
+GDN_DIM = 128
+
+
+@dataclass
+class GdnPlan:
+    n: int
+    parent_slot: np.ndarray     # [n] int32
+    segments: np.ndarray        # [n_segments, 4] int32: first chunk, chunk count, parent state slot, own state slot
+    chunks: np.ndarray          # [n_chunks, 2] int32: first slot, length
+    depth_offsets: np.ndarray   # [n_depths + 1] int32
+    n_states: int               # chains whose final state is kept (those with children)
+
+    @property
+    def n_segments(self) -> int:
+        return int(self.segments.shape[0])
+
+    @property
+    def n_chunks(self) -> int:
+        return int(self.chunks.shape[0])
+
+    @property
+    def n_depths(self) -> int:
+        return int(self.depth_offsets.shape[0]) - 1
+
+    def device_tables(self, device):
+        """(parent_slot, segments, chunks) as int32 device tensors."""
+        torch = _torch()
+        return tuple(torch.from_numpy(np.ascontiguousarray(a)).to(device)
+                     for a in (self.parent_slot, self.segments, self.chunks))
+
+
+def tree_gdn_plan(subtree_end, n: int) -> GdnPlan:
+    """Chains, chunks and depth buckets of the first ``n`` slots of a row (host)."""
+    se = np.ascontiguousarray(np.asarray(subtree_end)[:n], dtype=np.int32)
+    if len(se) != n:
+        raise ValueError("subtree_end shorter than n")
+    ns, nc, nd, nst = C.c_int64(0), C.c_int64(0), C.c_int64(0), C.c_int64(0)
+    _check(lib.tree_gdn_plan(n, _ptr(se, C.c_int32), None, None, 0, C.byref(ns), None, 0, C.byref(nc), None, 0,
+                             C.byref(nd), C.byref(nst)))
+    parent = np.empty(n, np.int32)
+    segs = np.empty((ns.value, 4), np.int32)
+    chunks = np.empty((nc.value, 2), np.int32)
+    offs = np.empty(nd.value + 1, np.int32)
+    _check(lib.tree_gdn_plan(n, _ptr(se, C.c_int32), _ptr(parent, C.c_int32), _ptr(segs, C.c_int32), ns.value,
+                             C.byref(ns), _ptr(chunks, C.c_int32), nc.value, C.byref(nc), _ptr(offs, C.c_int32),
+                             nd.value, C.byref(nd), C.byref(nst)))
+    return GdnPlan(n=n, parent_slot=parent, segments=segs, chunks=chunks, depth_offsets=offs, n_states=nst.value)
+
+
+def tree_gdn_workspace_bytes(n, n_states, n_chunks, Hk, Hv, dk=GDN_DIM, dv=GDN_DIM) -> int:
+    return int(lib.tree_gdn_workspace_bytes(n, n_states, n_chunks, Hk, Hv, dk, dv))
+
+
+def tree_gdn_fwd(x, conv_w, g, beta, plan: GdnPlan, Hk: int, Hv: int, out=None, ws=None, tables=None):
+    """Gated-delta-rule mixing over the plan's row.
+
+    x [>= n, C] bf16 (C = (2 Hk + Hv) 128, channels q | k | v), conv_w [C, W] fp32,
+    g, beta [>= n, Hv] fp32.  Returns out [n, Hv, 128] bf16 (``out`` may be given,
+    first dimension >= n).  ``tables``: device copies from plan.device_tables()."""
+    torch = _torch()
+    n = plan.n
+    Cc = (2 * Hk + Hv) * GDN_DIM
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != Cc or x.shape[0] < n:
+        raise ValueError(f"x must be bf16 [>= {n}, {Cc}]")
+    if conv_w.dtype != torch.float32 or conv_w.dim() != 2 or conv_w.shape[0] != Cc:
+        raise ValueError(f"conv_w must be fp32 [{Cc}, W]")
+    for t, nm in ((g, "g"), (beta, "beta")):
+        if t.dtype != torch.float32 or t.dim() != 2 or t.shape[1] != Hv or t.shape[0] < n:
+            raise ValueError(f"{nm} must be fp32 [>= {n}, {Hv}]")
+    if out is None:
+        out = torch.empty((n, Hv, GDN_DIM), dtype=torch.bfloat16, device=x.device)
+    if out.dtype != torch.bfloat16 or out.dim() != 3 or tuple(out.shape[1:]) != (Hv, GDN_DIM) or out.shape[0] < n:
+        raise ValueError(f"out must be bf16 [>= {n}, {Hv}, {GDN_DIM}]")
+    need = tree_gdn_workspace_bytes(n, plan.n_states, plan.n_chunks, Hk, Hv)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    par, segs, chunks = plan.device_tables(x.device) if tables is None else tables
+    offs = np.ascontiguousarray(plan.depth_offsets, dtype=np.int32)
+    _check(lib.tree_gdn_fwd(TREE_BF16, _dev(x, "x"), _dev(conv_w, "conv_w"), conv_w.shape[1], _dev(g, "g"),
+                            _dev(beta, "beta"), _dev(par, "parent_slot"), _dev(segs, "segments"), plan.n_segments,
+                            _dev(chunks, "chunks"), plan.n_chunks, _ptr(offs, C.c_int32), plan.n_depths,
+                            plan.n_states, n, Hk, Hv,
+                            GDN_DIM, GDN_DIM, _dev(out, "out"), ws.data_ptr(), ws.numel() * ws.element_size(),
+                            _stream()))
+    return out

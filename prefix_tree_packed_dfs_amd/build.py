@@ -25,6 +25,8 @@ SOURCES = [
     "attn_vec.hip",
     "attn_mfma_fwd.hip",
     "attn_mfma_bwd.hip",
+    "gdn_api.cpp",
+    "gdn.hip",
 ]
 
 # Packed-fp32 VALU ops are turned off for device code (the compiler would

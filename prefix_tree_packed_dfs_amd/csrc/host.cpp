@@ -31,7 +31,7 @@ void clear_error() { g_last_error[0] = '\0'; }
 
 using treeattn::fail;
 
-extern "C" int tree_abi_version(void) { return 2; }
+extern "C" int tree_abi_version(void) { return 3; }
 
 extern "C" const char* tree_status_string(int s) {
     switch (s) {
@@ -500,5 +500,108 @@ extern "C" tree_status tree_place_leaves(int32_t n_nodes, const int32_t* parent,
     if ((int64_t)tokens.size() > bins_cap)
         return fail(TREE_ERR_CAPACITY, "bins_cap %d < %zu rows", bins_cap, tokens.size());
     for (size_t b = 0; b < tokens.size(); ++b) bin_tokens[b] = (int32_t)tokens[b];
+    return TREE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// tree_gdn_plan
+//
+// A recurrent layer threads its state along each root-to-leaf path, forks it
+// at branch points and starts from zero at roots [ART "Token-mixing layers"].
+// In a DFS row the state passes from slot t-1 to slot t exactly when t-1 is
+// t's parent and has no other child, so the row splits into maximal runs of
+// consecutive slots (chains) that each start from one known state: zero at a
+// root, the final state of the chain ending at the parent otherwise.  Chains
+// are grouped by depth (number of chains above them): all chains of one depth
+// run together once every shallower chain is done, as the pages' planner
+// does with one pair of calls per depth.  Each chain is cut into chunks of up
+// to 64 slots starting at the chain's first slot.
+// ---------------------------------------------------------------------------
+
+extern "C" tree_status tree_gdn_plan(int64_t n, const int32_t* subtree_end, int32_t* parent_slot,
+                                     int32_t* segments, int64_t seg_cap, int64_t* n_segments,
+                                     int32_t* chunks, int64_t chunk_cap, int64_t* n_chunks,
+                                     int32_t* depth_offsets, int64_t depth_cap, int64_t* n_depths,
+                                     int64_t* n_states) {
+    treeattn::clear_error();
+    if (n < 0 || n > INT32_MAX) return fail(TREE_ERR_INVALID_ARG, "n = %lld", (long long)n);
+    if (n > 0 && !subtree_end) return fail(TREE_ERR_INVALID_ARG, "subtree_end is NULL");
+    if (!n_segments || !n_chunks || !n_depths || !n_states)
+        return fail(TREE_ERR_INVALID_ARG, "count outputs are NULL");
+    const tree_status vs = tree_validate_subtree_end(subtree_end, n);
+    if (vs != TREE_OK) return vs;
+    // parent of every slot: the innermost interval still open
+    std::vector<int32_t> par(n), nchild(n, 0);
+    {
+        std::vector<int32_t> open;
+        for (int32_t t = 0; t < (int32_t)n; ++t) {
+            while (!open.empty() && subtree_end[open.back()] < t) open.pop_back();
+            par[t] = open.empty() ? -1 : open.back();
+            if (par[t] >= 0) ++nchild[par[t]];
+            open.push_back(t);
+        }
+    }
+    // chains in slot order: start, length, parent chain, depth
+    std::vector<int32_t> seg_of(n), s_start, s_len, s_par, s_depth;
+    for (int32_t t = 0; t < (int32_t)n; ++t) {
+        const int32_t p = par[t];
+        if (p < 0 || p != t - 1 || nchild[p] > 1) {
+            const int32_t ps = p < 0 ? -1 : seg_of[p];
+            s_start.push_back(t);
+            s_len.push_back(0);
+            s_par.push_back(ps);
+            s_depth.push_back(ps < 0 ? 0 : s_depth[ps] + 1);
+        }
+        seg_of[t] = (int32_t)s_start.size() - 1;
+        ++s_len.back();
+    }
+    const int64_t ns = (int64_t)s_start.size();
+    int32_t max_depth = -1;
+    for (int32_t d : s_depth) max_depth = std::max(max_depth, d);
+    const int64_t nd = max_depth + 1;
+    // stable bucket sort by depth
+    std::vector<int64_t> off(nd + 1, 0);
+    for (int32_t d : s_depth) ++off[d + 1];
+    for (int64_t d = 0; d < nd; ++d) off[d + 1] += off[d];
+    std::vector<int32_t> order(ns);
+    {
+        std::vector<int64_t> fill(off.begin(), off.end() - 1);
+        for (int64_t s = 0; s < ns; ++s) order[fill[s_depth[s]]++] = (int32_t)s;
+    }
+    int64_t nc = 0;
+    for (int32_t L : s_len) nc += (L + 63) / 64;
+    // a saved final state only for chains with children, numbered in plan order
+    std::vector<uint8_t> has_kids(ns, 0);
+    for (int64_t s = 0; s < ns; ++s)
+        if (s_par[s] >= 0) has_kids[s_par[s]] = 1;
+    std::vector<int32_t> state_of(ns, -1);
+    int32_t nst = 0;
+    for (int64_t r = 0; r < ns; ++r)
+        if (has_kids[order[r]]) state_of[order[r]] = nst++;
+    *n_segments = ns;
+    *n_chunks = nc;
+    *n_depths = nd;
+    *n_states = nst;
+    if (!parent_slot && !segments && !chunks && !depth_offsets) return TREE_OK;  // size query
+    if (!parent_slot || !segments || !chunks || !depth_offsets)
+        return fail(TREE_ERR_INVALID_ARG, "some plan outputs are NULL");
+    if (ns > seg_cap || nc > chunk_cap || nd > depth_cap)
+        return fail(TREE_ERR_CAPACITY, "plan needs %lld chains, %lld chunks, %lld depths", (long long)ns,
+                    (long long)nc, (long long)nd);
+    std::copy(par.begin(), par.end(), parent_slot);
+    int64_t c = 0;
+    for (int64_t r = 0; r < ns; ++r) {
+        const int32_t s = order[r];
+        const int32_t k = (s_len[s] + 63) / 64;
+        segments[4 * r + 0] = (int32_t)c;
+        segments[4 * r + 1] = k;
+        segments[4 * r + 2] = s_par[s] < 0 ? -1 : state_of[s_par[s]];
+        segments[4 * r + 3] = state_of[s];
+        for (int32_t j = 0; j < k; ++j, ++c) {
+            chunks[2 * c + 0] = s_start[s] + 64 * j;
+            chunks[2 * c + 1] = std::min(64, s_len[s] - 64 * j);
+        }
+    }
+    for (int64_t d = 0; d <= nd; ++d) depth_offsets[d] = (int32_t)off[d];
     return TREE_OK;
 }
