@@ -300,6 +300,90 @@ def bench_sweep(args):
                       "dtype": "bf16", "data": "synthetic", "points": rows}), flush=True)
 
 
+def bench_gdn(args):
+    """Gated-delta-rule mixing (tree_gdn_fwd) on the packed row and on sequence packing.
+
+    Layer shape: 16 key heads, 32 value heads, head dims 128, convolution width 4.  Inputs
+    (x, g, beta) are resident in HBM and the plan's device tables are uploaded before timing;
+    a step is one tree_gdn_fwd call.  The oracle (fp64, per sequence) is timed on the first
+    sequence for two value heads and scaled to the row by raw tokens and heads.  Prints one
+    JSON line."""
+    import numpy as np
+    import torch
+
+    import prefix_tree_packed_dfs_amd as lib
+    from synth import agentic_trie, grpo_group, long_history, sequence_packing_forest
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    Hk, Hv, W = 16, 32, 4
+    C = (2 * Hk + Hv) * 128
+    names = args.gdn_workloads.split(",")
+    makers = {"grpo_group": grpo_group, "agentic_trie": agentic_trie, "long_history": long_history}
+    g0 = torch.Generator(device=dev).manual_seed(11)
+    conv_w = (torch.randn((C, W), generator=g0, device=dev) / 2.0).contiguous()
+    rows = []
+    for name in names:
+        w = makers[name]()
+        res = {"workload": name, "sequences": len(w.sequences), "raw_tokens": w.raw_tokens}
+        for layout in ("tree", "sequence_packing"):
+            if layout == "tree":
+                parent, seq_last = lib.tree_build_trie(w.sequences, min_shared=64)
+            else:
+                parent, seq_last = sequence_packing_forest(w.sequences)
+            n = len(parent)
+            lay = lib.tree_pack_layout(parent, seq_last, n)
+            plan = lib.tree_gdn_plan(lay.subtree_end, n)
+            tables = plan.device_tables(dev)
+            x = torch.randn((n, C), generator=g0, device=dev).to(torch.bfloat16)
+            g = -0.1 * torch.rand((n, Hv), generator=g0, device=dev)
+            beta = torch.rand((n, Hv), generator=g0, device=dev)
+            out = torch.empty((n, Hv, 128), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(lib.tree_gdn_workspace_bytes(n, plan.n_states, plan.n_chunks, Hk, Hv), dtype=torch.uint8,
+                             device=dev)
+            for _ in range(args.warmup):
+                lib.tree_gdn_fwd(x, conv_w, g, beta, plan, Hk, Hv, out=out, ws=ws, tables=tables)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                lib.tree_gdn_fwd(x, conv_w, g, beta, plan, Hk, Hv, out=out, ws=ws, tables=tables)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            res[layout] = {"slots": n, "chains": plan.n_segments, "chunks": plan.n_chunks, "depths": plan.n_depths,
+                           "ms_per_call": round(ms, 4), "slots_per_s": round(n / (ms * 1e-3), 1),
+                           "raw_tok_s": round(w.raw_tokens / (ms * 1e-3), 1),
+                           "workspace_bytes": int(ws.numel())}
+            print(f"# gdn {name} {layout}: {n} slots, {plan.n_segments} chains, {plan.n_depths} depths, "
+                  f"{ms:.3f} ms", file=sys.stderr, flush=True)
+            del x, g, beta, out, ws, tables
+        res["packing_ratio"] = round(w.raw_tokens / res["tree"]["slots"], 4)
+        res["speedup"] = round(res["sequence_packing"]["ms_per_call"] / res["tree"]["ms_per_call"], 3)
+        rows.append(res)
+    rec = {"metric": "gated-delta-rule mixing over packed rows: raw tokens/s, tree vs sequence packing",
+           "unit": "tokens/s", "value": rows[0]["tree"]["raw_tok_s"], "steps": args.steps, "warmup": args.warmup,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": rows[0]["workload"], "Hk": Hk, "Hv": Hv, "dk": 128, "dv": 128, "conv_width": W},
+           "points": rows}
+    if not args.no_cpu_baseline:
+        from oracle.gdn import GdnShape, tree_gdn
+        from synth import gdn_tables
+        w = makers[names[0]]()
+        t = gdn_tables(w, Hk=Hk, Hv=Hv, conv_width=W)
+        heads = [0, Hv - 1]
+        t0 = time.perf_counter()
+        tree_gdn(w.sequences, w.fid, t, t["conv_w"], GdnShape(Hk, Hv, 128, 128), storage="bf16", heads=heads, seqs=[0])
+        dt = time.perf_counter() - t0
+        frac = len(w.sequences[0]) / w.raw_tokens * len(heads) / Hv
+        rec["cpu_baseline"] = {"value": round(w.raw_tokens / (dt / frac), 1), "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"oracle GDN on sequence 0 ({len(w.sequences[0])} of {w.raw_tokens} raw "
+                                         f"tokens), value heads {heads} of {Hv}: {dt:.2f} s, scaled by "
+                                         f"{1 / frac:.0f}x"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,7 +398,16 @@ def main():
                     help="only time the host row planner (trie walk + leaf placement) on curriculum batches")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the tree-vs-sequence-packing sweep over packing ratios 1.0 .. 4.9")
+    ap.add_argument("--gdn", action="store_true",
+                    help="only time gated-delta-rule mixing (tree and sequence packing) on the bf16 workloads")
+    ap.add_argument("--gdn-workloads", default="grpo_group,agentic_trie,long_history")
     args = ap.parse_args()
+    if args.gdn:
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_gdn(args)
+        return
     if args.sweep:
         if args.gpus != 1:
             print("bench.py runs on one GPU only", file=sys.stderr)

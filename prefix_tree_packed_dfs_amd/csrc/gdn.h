@@ -10,20 +10,22 @@ namespace treeattn {
 constexpr int kGdnChunk = 64;   // tokens per chunk of the chunked recurrence
 constexpr int kGdnDim = 128;    // key and value head dim
 
-// Per (chunk, value head) block written by the chunk kernel and read by the
-// state pass: operand fragments in the lane order the matrix core reads them.
+// Per (chunk, value head) block written by the chunk kernel and copied whole into
+// LDS by the state pass: operand fragments in the lane order the matrix core reads.
 //   Wn  [2 row tiles][8 K-steps][64 lanes][8]  bf16   -W, A operand of W H
-//   U   [4 col tiles][2 row tiles][64][16]     bf16   U, accumulator layout
 //   M   [2 row tiles][4 K-steps][64][8]        bf16   decayed, masked Q K^T, A operand
 //   KT  [4 row tiles][4 K-steps][64][8]        bf16   K^T, A operand of the state update
-//   eG  [64] fp32 e^{G_i}; eLG [64] fp32 e^{G_last - G_j}
+//   Q   [2 row tiles][8 K-steps][64][8]        bf16   diag(e^G) Q, A operand of Q H
+//   U   [4 col tiles][2 row tiles][64][16]     bf16   U, accumulator layout
+//   eLG [64] fp32 e^{G_last - G_j}; gL fp32 e^{G_last}
 constexpr size_t kGdnWn = 0;
-constexpr size_t kGdnU = kGdnWn + 2 * 8 * 64 * 8 * 2;
-constexpr size_t kGdnM = kGdnU + 4 * 2 * 64 * 16 * 2;
+constexpr size_t kGdnM = kGdnWn + 2 * 8 * 64 * 8 * 2;
 constexpr size_t kGdnKT = kGdnM + 2 * 4 * 64 * 8 * 2;
-constexpr size_t kGdnEG = kGdnKT + 4 * 4 * 64 * 8 * 2;
-constexpr size_t kGdnELG = kGdnEG + 64 * 4;
-constexpr size_t kGdnBlock = kGdnELG + 64 * 4;
+constexpr size_t kGdnQ = kGdnKT + 4 * 4 * 64 * 8 * 2;
+constexpr size_t kGdnU = kGdnQ + 2 * 8 * 64 * 8 * 2;
+constexpr size_t kGdnELG = kGdnU + 4 * 2 * 64 * 16 * 2;
+constexpr size_t kGdnGL = kGdnELG + 64 * 4;
+constexpr size_t kGdnBlock = kGdnGL + 256;  // 74,240 bytes
 
 struct GdnArgs {
     const void* x;            // [n, C] bf16 mixing input, channels q | k | v
