@@ -205,6 +205,7 @@ tree_status tree_validate_subtree_end(const int32_t* subtree_end, int64_t n);
  * path neighbouring tokens are one position apart.  Rotate-half pairing:
  * dimensions i and i + D/2 rotate by pos * theta^(-2i/D), i < D/2.  Angles
  * and sines are taken in fp64 and the result is rounded once to `dt`.
+ * Slots at depth 0 are the identity and are left untouched.
  *
  *   x        [B, N, H, D] of dtype dt, rotated in place
  *   pos_ids  [B, N] int32 (tree_pack_layout's pos_ids per row)

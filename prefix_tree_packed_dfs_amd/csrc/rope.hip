@@ -10,6 +10,8 @@
 // and cosines are computed once and reused H times.  They are computed in fp64
 // (the angle reaches tens of thousands of radians at depth 36K, where an fp32
 // angle would already be off by ~1e-3) and rounded once to the storage type.
+// A slot at depth 0 (a root, or a padding slot) turns by angle 0, which is the
+// identity, so its rows are neither read nor written.
 #include "common.h"
 #include "device.h"
 
@@ -26,7 +28,9 @@ __global__ __launch_bounds__(256) void rope_kernel_bf16(__bf16* __restrict__ x, 
     const int64_t slot = gid / QUADS;
     const int quad = (int)(gid % QUADS);
     if (slot >= BN) return;
-    const double p = (double)pos[slot];
+    const int p_i = pos[slot];
+    if (p_i == 0) return;  // identity
+    const double p = (double)p_i;
     float c[4], s[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -41,17 +45,36 @@ __global__ __launch_bounds__(256) void rope_kernel_bf16(__bf16* __restrict__ x, 
     // fp32 products are enough for bf16 storage: one rounding of an fp32
     // expression whose error is far below half a bf16 ulp.
     __bf16* row = x + slot * (int64_t)H * D + quad * 4;
-    for (int h = 0; h < H; ++h) {
-        bf16x4* a = reinterpret_cast<bf16x4*>(row + (int64_t)h * D);
-        bf16x4* b = reinterpret_cast<bf16x4*>(row + (int64_t)h * D + HALF);
-        const bf16x4 va = *a, vb = *b;
-        bf16x4 ra, rb;
+    auto rotate = [&](const bf16x4& va, const bf16x4& vb, bf16x4& ra, bf16x4& rb) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const float xa = (float)va[u], xb = (float)vb[u];
             ra[u] = (__bf16)(xa * c[u] - xb * s[u]);
             rb[u] = (__bf16)(xb * c[u] + xa * s[u]);
         }
+    };
+    // heads in groups of four: all loads of a group are in flight together
+    int h = 0;
+    for (; h + 4 <= H; h += 4) {
+        bf16x4 va[4], vb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            va[e] = *reinterpret_cast<const bf16x4*>(row + (int64_t)(h + e) * D);
+            vb[e] = *reinterpret_cast<const bf16x4*>(row + (int64_t)(h + e) * D + HALF);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bf16x4 ra, rb;
+            rotate(va[e], vb[e], ra, rb);
+            *reinterpret_cast<bf16x4*>(row + (int64_t)(h + e) * D) = ra;
+            *reinterpret_cast<bf16x4*>(row + (int64_t)(h + e) * D + HALF) = rb;
+        }
+    }
+    for (; h < H; ++h) {
+        bf16x4* a = reinterpret_cast<bf16x4*>(row + (int64_t)h * D);
+        bf16x4* b = reinterpret_cast<bf16x4*>(row + (int64_t)h * D + HALF);
+        bf16x4 ra, rb;
+        rotate(*a, *b, ra, rb);
         *a = ra;
         *b = rb;
     }
@@ -69,7 +92,9 @@ __global__ __launch_bounds__(256) void rope_kernel_f32(float* __restrict__ x,
     const int64_t slot = gid / QUADS;
     const int quad = (int)(gid % QUADS);
     if (slot >= BN) return;
-    const double p = (double)pos[slot];
+    const int p_i = pos[slot];
+    if (p_i == 0) return;  // identity
+    const double p = (double)p_i;
     double c[4], s[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
