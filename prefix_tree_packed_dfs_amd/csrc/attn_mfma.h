@@ -21,6 +21,7 @@ inline bool mfma_supported(int D, int G) {
 struct FwdWorkspace {
     int32_t* tile_min;   // [B, T]
     int32_t* tile_max;   // [B, T]
+    int32_t* tile_iso;   // [B, T] 1 if every slot of the tile is isolated (sees and is seen by itself only)
 };
 
 // Workspace carved by the backward.
@@ -29,6 +30,7 @@ struct BwdWorkspace {
     float* lse2;         // [B, Hq, N]  lse * log2(e)
     int32_t* tile_min;   // [B, T]
     int32_t* tile_max;   // [B, T]
+    int32_t* tile_iso;   // [B, T]
     // dK/dV work plan: KV tiles of 256 keys whose query range is long are split
     // into chunks of visits; chunks write fp32 partials that a reduce pass sums
     int32_t* ctrl;       // queue counters / lengths / starts, split-tile count
@@ -44,8 +46,12 @@ constexpr int kKvTile = 256;
 constexpr int kSplitSlots = 1536 * 256 / kKvTile;
 constexpr int kVisitBudget = 96;
 
-// Smallest and largest subtree_end of every KT-key tile of each row ([B, T]).
-hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, int32_t* tmax, hipStream_t st);
+// Smallest and largest subtree_end of every KT-key tile of each row ([B, T]),
+// and whether every slot of the tile is isolated.
+hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, int32_t* tmax, int32_t* tiso,
+                              hipStream_t st);
+// Gradient rows of the isolated slots (dq = dk = 0, dv = sum of the group's dout rows).
+hipError_t launch_isolated_bwd(const AttnArgs& a, const int32_t* tiso, hipStream_t st);
 size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D);
 FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D);
 hipError_t mfma_attn_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st);

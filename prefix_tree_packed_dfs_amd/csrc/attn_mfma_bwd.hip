@@ -84,9 +84,10 @@ __device__ int block_exclusive_scan(int v, int* s_scan) {
     return r;
 }
 
-__global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tmax, int B, int N, int T, int G,
-                                                 int Hkv, int* __restrict__ ctrl, int4* __restrict__ tile_plan,
-                                                 int4* __restrict__ units, int4* __restrict__ split_tiles) {
+__global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tmax, const int32_t* __restrict__ tiso,
+                                                 int B, int N, int T, int G, int Hkv, int* __restrict__ ctrl,
+                                                 int4* __restrict__ tile_plan, int4* __restrict__ units,
+                                                 int4* __restrict__ split_tiles) {
     __shared__ int s_sum, s_budget;
     __shared__ int s_scan[1024];
     __shared__ int s_cnt[kPlanBuckets];
@@ -96,11 +97,15 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
     constexpr int SUB = kKvTile / KT, BPT = kKvTile / 32;  // 64-key tiles, 32-key blocks per KV tile
     const int NB = (N + 31) / 32;
     const int NQ = Hkv < 8 ? Hkv : 8;
+    // a tile of isolated keys gets no units (bwd_isolated writes its gradients)
     for (int u = tid; u < BT; u += 1024) {
         const int b = u / TT, t = u % TT;
-        int qmax = -1;
-        for (int x = SUB * t; x < min(SUB * t + SUB, T); ++x) qmax = max(qmax, tmax[(int64_t)b * T + x]);
-        tile_plan[u] = make_int4(BPT * t, max(qmax / 32, BPT * t), 1, -1);
+        int qmax = -1, iso = 1;
+        for (int x = SUB * t; x < min(SUB * t + SUB, T); ++x) {
+            qmax = max(qmax, tmax[(int64_t)b * T + x]);
+            iso &= tiso[(int64_t)b * T + x];
+        }
+        tile_plan[u] = iso ? make_int4(BPT * t, BPT * t, 0, -1) : make_int4(BPT * t, max(qmax / 32, BPT * t), 1, -1);
     }
     if (tid == 0) s_budget = kVisitBudget;
     __syncthreads();
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
     int my_chunks = 0, my_split = 0, my_units = 0;
     for (int u = u0; u < u1; ++u) {
         const int4 e = tile_plan[u];
-        const int nc = e.y - e.x + 1 > C ? e.y / C - e.x / C + 1 : 1;
+        const int nc = e.z == 0 ? 0 : e.y - e.x + 1 > C ? e.y / C - e.x / C + 1 : 1;
         if (nc > 1) {
             my_chunks += nc;
             my_split += 1;
@@ -147,7 +152,7 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
         int slot = packed & 0xFFFF, z = packed >> 16;
         for (int u = u0; u < u1; ++u) {
             int4 e = tile_plan[u];
-            const int nc = e.y - e.x + 1 > C ? e.y / C - e.x / C + 1 : 1;
+            const int nc = e.z == 0 ? 0 : e.y - e.x + 1 > C ? e.y / C - e.x / C + 1 : 1;
             if (nc > 1) {
                 e.z = nc;
                 e.w = slot;
@@ -554,6 +559,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
                                                  float* __restrict__ delta, float* __restrict__ lse2,
                                                  const int32_t* __restrict__ se,
                                                  const int32_t* __restrict__ tmin, const int32_t* __restrict__ tmax,
+                                                 const int32_t* __restrict__ tiso,
                                                  int B, int N, int Hq, int Hkv, int T, int n_qtiles, int n_chunks,
                                                  float scale_log2, float scale, __bf16* __restrict__ dq) {
     constexpr int BM = 256 / HB;
@@ -629,6 +635,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
     // wait for them is not placed inside the tile loop (where it would drain
     // the prefetches of later tiles)
     wait_vmcnt<0>();
+    {
+        // a block of isolated slots only: dq = 0 is written by bwd_isolated
+        int iso = 1;
+        for (int t = i0 / KT; t <= t_last; ++t) iso &= tiso[(int64_t)b * T + t];
+        if (iso) return;
+    }
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) zero(acc[db]);
@@ -785,7 +797,7 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
     hipLaunchKernelGGL((bwd_dq<D, HB>), dim3((unsigned)blocks), dim3(512), 0, st, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.out, (const __bf16*)a.dout, a.lse,
                        w.delta, w.lse2, a.se,
-                       w.tile_min, w.tile_max, a.B, a.N, a.Hq, a.Hkv, T, n_qtiles,
+                       w.tile_min, w.tile_max, w.tile_iso, a.B, a.N, a.Hq, a.Hkv, T, n_qtiles,
                        n_chunks, a.scale * kLog2e, a.scale, (__bf16*)a.dq);
     return hipGetLastError();
 }
@@ -793,10 +805,10 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
 template <int D>
 hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
-    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, st);
+    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, w.tile_iso, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_plan, dim3(1), dim3(1024), 0, st, w.tile_max, a.B, a.N, T, a.Hq / a.Hkv, a.Hkv, w.ctrl,
-                       w.tile_plan, w.units, w.split_tiles);
+    hipLaunchKernelGGL(bwd_plan, dim3(1), dim3(1024), 0, st, w.tile_max, w.tile_iso, a.B, a.N, T, a.Hq / a.Hkv,
+                       a.Hkv, w.ctrl, w.tile_plan, w.units, w.split_tiles);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // dQ first: it also writes delta and lse * log2(e), which dK/dV reads
@@ -815,7 +827,10 @@ hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) 
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_reduce<D>), dim3(kSplitSlots / 2, kKvTile / 32), dim3(256), 0, st, w.ctrl,
                        w.split_tiles, w.partial, a.N, a.Hkv, (__bf16*)a.dk, (__bf16*)a.dv);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // last: exact rows of the isolated slots (over whatever the kernels above wrote for them)
+    return launch_isolated_bwd(a, w.tile_iso, st);
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -832,7 +847,7 @@ size_t plan_bytes(int B, int N, int Hkv, int D) {
 
 size_t mfma_bwd_ws_bytes(int B, int N, int Hq, int Hkv, int D) {
     const size_t T = (size_t)(N + KT - 1) / KT;
-    return 2 * align256((size_t)B * Hq * N * sizeof(float)) + 2 * align256((size_t)B * T * sizeof(int32_t)) +
+    return 2 * align256((size_t)B * Hq * N * sizeof(float)) + 3 * align256((size_t)B * T * sizeof(int32_t)) +
            plan_bytes(B, N, Hkv, D);
 }
 
@@ -847,6 +862,8 @@ BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D) {
     w.tile_min = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)B * T * sizeof(int32_t));
     w.tile_max = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)B * T * sizeof(int32_t));
+    w.tile_iso = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)B * T * sizeof(int32_t));
     const size_t TT = (size_t)(N + kKvTile - 1) / kKvTile;
     const size_t ucap = (size_t)kSplitSlots + (size_t)B * TT * Hkv;

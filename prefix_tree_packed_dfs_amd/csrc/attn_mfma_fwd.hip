@@ -37,19 +37,150 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994531f;
 
-// Smallest and largest subtree_end of every 64-key tile: grid (ceil(T / 4), B),
-// 256 threads, one wave per tile.
+// Smallest and largest subtree_end of every 64-key tile, and whether every key
+// of the tile is seen by itself only (subtree_end[j] == j): grid (ceil(T / 4),
+// B), 256 threads, one wave per tile.
 __global__ __launch_bounds__(256) void fwd_prep(const int32_t* __restrict__ se, int N, int T,
-                                                int32_t* __restrict__ tmin, int32_t* __restrict__ tmax) {
+                                                int32_t* __restrict__ tmin, int32_t* __restrict__ tmax,
+                                                int32_t* __restrict__ tiso) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6), b = blockIdx.y, lane = threadIdx.x & 63;
     if (t >= T) return;
     const int j = t * KT + lane;
     const int s = j < N ? se[(int64_t)b * N + j] : -1;
     const int mn = wave_min_i32(j < N ? s : INT_MAX);
     const int mx = wave_max_i32(s);
+    const bool self_only = __ballot(j < N && s != j) == 0;
     if (lane == 0) {
         tmin[(int64_t)b * T + t] = mn;
         tmax[(int64_t)b * T + t] = mx;
+        tiso[(int64_t)b * T + t] = self_only ? 1 : 0;
+    }
+}
+
+// A slot is isolated when it is a root without descendants: no interval
+// [j, subtree_end[j]] other than its own contains it, so as a query it sees only
+// itself and as a key it is seen only by itself (the padding after the packed
+// tokens of a row, one-token sequences).  A tile of keys seen by themselves
+// only is isolated when no key before the tile reaches into it, i.e. the
+// largest subtree_end before the tile is below its first slot.  Grid (B), 1024
+// threads; a running maximum over the tiles, 1024 per step.
+__global__ __launch_bounds__(1024) void iso_scan(const int32_t* __restrict__ tmax, int T,
+                                                 int32_t* __restrict__ tiso) {
+    __shared__ int s_wave[16];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int carry = -1;  // largest subtree_end of the tiles before this step's
+    for (int c0 = 0; c0 < T; c0 += 1024) {
+        const int t = c0 + tid;
+        int v = t < T ? tmax[(int64_t)b * T + t] : -1;
+        // inclusive running maximum: inside the wave, then over the waves
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(v, off, 64);
+            if (lane >= off) v = max(v, y);
+        }
+        if (lane == 63) s_wave[wave] = v;
+        __syncthreads();
+        if (wave == 0) {
+            int w = lane < 16 ? s_wave[lane] : -1;
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+                const int y = __shfl_up(w, off, 64);
+                if (lane >= off) w = max(w, y);
+            }
+            if (lane < 16) s_wave[lane] = w;
+        }
+        __syncthreads();
+        const int incl = max(v, wave > 0 ? s_wave[wave - 1] : -1);
+        const int prev = __shfl_up(incl, 1, 64);
+        const int before = max(carry, lane > 0 ? prev : (wave > 0 ? s_wave[wave - 1] : -1));
+        if (t < T) {
+            int* f = tiso + (int64_t)b * T + t;
+            *f = (*f && before < t * KT) ? 1 : 0;
+        }
+        carry = max(carry, s_wave[15]);
+        __syncthreads();
+    }
+}
+
+// Isolated slots of the forward: a query that sees only itself has a one-term
+// softmax, so out = v and lse = scale q.k.  Grid (T, kIsoSplit, B), 256
+// threads; tiles that are not isolated return at once.  The (slot, head) rows
+// of a tile are split over kIsoSplit workgroups, D / 8 lanes per row.
+constexpr int kIsoSplit = 8;
+
+template <int D>
+__global__ __launch_bounds__(256) void fwd_isolated(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                    const __bf16* __restrict__ v, const int32_t* __restrict__ tiso,
+                                                    int N, int Hq, int Hkv, int T, float scale,
+                                                    __bf16* __restrict__ out, float* __restrict__ lse) {
+    const int t = blockIdx.x, b = blockIdx.z;
+    if (!tiso[(int64_t)b * T + t]) return;
+    constexpr int LPR = D / 8, RPW = 64 / LPR;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int G = Hq / Hkv, rows = KT * Hq / kIsoSplit, rbase = blockIdx.y * rows;
+    const int e = (lane % LPR) * 8;
+#pragma unroll 4
+    for (int r0 = rbase + wave * RPW; r0 < rbase + rows; r0 += 4 * RPW) {
+        const int r = r0 + lane / LPR;
+        const int slot = t * KT + r / Hq, h = r % Hq;
+        const int sc = min(slot, N - 1);
+        const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(q + (((int64_t)b * N + sc) * Hq + h) * D + e);
+        const int64_t kv = (((int64_t)b * N + sc) * Hkv + h / G) * D + e;
+        const bf16x8 k8 = *reinterpret_cast<const bf16x8*>(k + kv);
+        const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(v + kv);
+        float dot = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dot = fmaf((float)q8[i], (float)k8[i], dot);
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o, 64);
+        if (slot < N) {
+            *reinterpret_cast<bf16x8*>(out + (((int64_t)b * N + slot) * Hq + h) * D + e) = v8;
+            if (lane % LPR == 0) lse[((int64_t)b * Hq + h) * N + slot] = dot * scale;
+        }
+    }
+}
+
+// Isolated slots of the backward: P = 1 on the diagonal and nothing else, so
+// dS = P (dP - delta) = dout.v - dout.out = 0: dq = dk = 0, and dv is the sum of
+// the dout rows of the query heads sharing the key's head.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_isolated(const __bf16* __restrict__ dout,
+                                                    const int32_t* __restrict__ tiso, int N, int Hq, int Hkv,
+                                                    int T, __bf16* __restrict__ dq, __bf16* __restrict__ dk,
+                                                    __bf16* __restrict__ dv) {
+    const int t = blockIdx.x, b = blockIdx.z;
+    if (!tiso[(int64_t)b * T + t]) return;
+    constexpr int LPR = D / 8, RPW = 64 / LPR;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int G = Hq / Hkv;
+    const int e = (lane % LPR) * 8;
+    const bf16x8 z = {};
+    const int qrows = KT * Hq / kIsoSplit, qbase = blockIdx.y * qrows;
+#pragma unroll 4
+    for (int r0 = qbase + wave * RPW; r0 < qbase + qrows; r0 += 4 * RPW) {  // dq rows
+        const int r = r0 + lane / LPR;
+        const int slot = t * KT + r / Hq;
+        if (slot < N) *reinterpret_cast<bf16x8*>(dq + (((int64_t)b * N + slot) * Hq + r % Hq) * D + e) = z;
+    }
+    const int kvrows = KT * Hkv / kIsoSplit, kvbase = blockIdx.y * kvrows;
+#pragma unroll 4
+    for (int r0 = kvbase + wave * RPW; r0 < kvbase + kvrows; r0 += 4 * RPW) {  // dk, dv rows
+        const int r = r0 + lane / LPR;
+        const int slot = t * KT + r / Hkv, g = r % Hkv;
+        if (slot >= N) continue;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const __bf16* src = dout + (((int64_t)b * N + slot) * Hq + (int64_t)g * G) * D + e;
+        for (int h = 0; h < G; ++h) {
+            const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(src + (int64_t)h * D);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += (float)d8[i];
+        }
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (__bf16)acc[i];
+        const int64_t kv = (((int64_t)b * N + slot) * Hkv + g) * D + e;
+        *reinterpret_cast<bf16x8*>(dk + kv) = z;
+        *reinterpret_cast<bf16x8*>(dv + kv) = o;
     }
 }
 
@@ -57,7 +188,8 @@ template <int D, int HB>
 __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                    const __bf16* __restrict__ v, const int32_t* __restrict__ se,
                                                    const int32_t* __restrict__ tmin,
-                                                   const int32_t* __restrict__ tmax, int B, int N, int Hq,
+                                                   const int32_t* __restrict__ tmax,
+                                                   const int32_t* __restrict__ tiso, int B, int N, int Hq,
                                                    int Hkv, int T, int n_qtiles, int n_chunks, float scale_log2,
                                                    __bf16* __restrict__ out, float* __restrict__ lse) {
     constexpr int BM = 256 / HB;          // positions per workgroup (8 waves x 32 rows = BM x HB)
@@ -91,6 +223,12 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
     const int i0 = qt * BM;
     const int i_last = min(i0 + BM, N) - 1;
     const int t_last = i_last / KT;
+    {
+        // a block of isolated slots only is written by fwd_isolated
+        int iso = 1;
+        for (int t = i0 / KT; t <= t_last; ++t) iso &= tiso[(int64_t)b * T + t];
+        if (iso) return;
+    }
     const int32_t* tmaxb = tmax + (int64_t)b * T;
     const int32_t* tminb = tmin + (int64_t)b * T;
     const int32_t* seb = se + (int64_t)b * N;
@@ -317,7 +455,8 @@ hipError_t launch_main(const AttnArgs& a, const FwdWorkspace& w, int T, hipStrea
     const int64_t blocks = (int64_t)n_qtiles * a.B * a.Hkv * n_chunks;
     const float scale_log2 = a.scale * 1.4426950408889634f;
     hipLaunchKernelGGL((fwd_main<D, HB>), dim3((unsigned)blocks), dim3(512), 0, st, (const __bf16*)a.q,
-                       (const __bf16*)a.k, (const __bf16*)a.v, a.se, w.tile_min, w.tile_max, a.B, a.N, a.Hq,
+                       (const __bf16*)a.k, (const __bf16*)a.v, a.se, w.tile_min, w.tile_max, w.tile_iso, a.B,
+                       a.N, a.Hq,
                        a.Hkv, T, n_qtiles, n_chunks, scale_log2, (__bf16*)a.out, a.lse);
     return hipGetLastError();
 }
@@ -325,14 +464,20 @@ hipError_t launch_main(const AttnArgs& a, const FwdWorkspace& w, int T, hipStrea
 template <int D>
 hipError_t launch_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
-    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, st);
+    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, w.tile_iso, st);
     if (e != hipSuccess) return e;
     switch (heads_per_wg(a.Hq / a.Hkv)) {
-        case 1: return launch_main<D, 1>(a, w, T, st);
-        case 2: return launch_main<D, 2>(a, w, T, st);
-        case 4: return launch_main<D, 4>(a, w, T, st);
-        default: return launch_main<D, 8>(a, w, T, st);
+        case 1: e = launch_main<D, 1>(a, w, T, st); break;
+        case 2: e = launch_main<D, 2>(a, w, T, st); break;
+        case 4: e = launch_main<D, 4>(a, w, T, st); break;
+        default: e = launch_main<D, 8>(a, w, T, st); break;
     }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fwd_isolated<D>), dim3((unsigned)T, kIsoSplit, (unsigned)a.B), dim3(256), 0, st,
+                       (const __bf16*)a.q,
+                       (const __bf16*)a.k, (const __bf16*)a.v, w.tile_iso, a.N, a.Hq, a.Hkv, T, a.scale,
+                       (__bf16*)a.out, a.lse);
+    return hipGetLastError();
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -343,7 +488,7 @@ size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D) {
     (void)Hkv;
     (void)D;
     const size_t T = (size_t)(N + KT - 1) / KT;
-    return 2 * align256((size_t)B * T * sizeof(int32_t));
+    return 3 * align256((size_t)B * T * sizeof(int32_t));
 }
 
 FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D) {
@@ -355,12 +500,31 @@ FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D) {
     w.tile_min = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)B * T * sizeof(int32_t));
     w.tile_max = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)B * T * sizeof(int32_t));
+    w.tile_iso = reinterpret_cast<int32_t*>(p);
     return w;
 }
 
-hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, int32_t* tmax, hipStream_t st) {
+hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, int32_t* tmax, int32_t* tiso,
+                              hipStream_t st) {
     const int T = (N + KT - 1) / KT;
-    hipLaunchKernelGGL(fwd_prep, dim3((T + 3) / 4, B), dim3(256), 0, st, se, N, T, tmin, tmax);
+    hipLaunchKernelGGL(fwd_prep, dim3((T + 3) / 4, B), dim3(256), 0, st, se, N, T, tmin, tmax, tiso);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(iso_scan, dim3(B), dim3(1024), 0, st, tmax, T, tiso);
+    return hipGetLastError();
+}
+
+hipError_t launch_isolated_bwd(const AttnArgs& a, const int32_t* tiso, hipStream_t st) {
+    const int T = (a.N + KT - 1) / KT;
+    if (a.D == 64)
+        hipLaunchKernelGGL((bwd_isolated<64>), dim3((unsigned)T, kIsoSplit, (unsigned)a.B), dim3(256), 0, st,
+                           (const __bf16*)a.dout, tiso, a.N, a.Hq, a.Hkv, T, (__bf16*)a.dq, (__bf16*)a.dk,
+                           (__bf16*)a.dv);
+    else
+        hipLaunchKernelGGL((bwd_isolated<128>), dim3((unsigned)T, kIsoSplit, (unsigned)a.B), dim3(256), 0, st,
+                           (const __bf16*)a.dout, tiso, a.N, a.Hq, a.Hkv, T, (__bf16*)a.dq, (__bf16*)a.dk,
+                           (__bf16*)a.dv);
     return hipGetLastError();
 }
 

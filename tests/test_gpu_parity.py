@@ -234,3 +234,87 @@ def test_batch_rows_are_independent_and_deterministic():
                                se[b:b + 1].contiguous(), o1, l1, do[b:b + 1].contiguous())
         for x, y in zip(g1, grads):
             assert torch.allclose(x[0].float(), y[b].float(), atol=1e-2, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# isolated slots (each sees only itself): one-token sequences and padding
+# ---------------------------------------------------------------------------
+
+def _trees_around_singles(seed, n_single):
+    """Two random tries with n_single one-token sequences between them in the DFS order (roots are
+    ordered by first token): long runs of isolated slots, so whole query blocks and key tiles of the
+    kernels hold nothing else, next to blocks that mix them with tree tokens."""
+    rng = np.random.default_rng(seed)
+    seqs = []
+    for lo in (0, 50_000):
+        for _ in range(4):
+            L = int(rng.integers(60, 400))
+            s = np.repeat(rng.integers(0, 2, size=L // 40 + 1), 40)[:L].astype(np.int32) + lo
+            seqs.append(s)
+    singles = [np.array([1000 + i], np.int32) for i in range(n_single)]
+    return seqs[:4] + singles + seqs[4:]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(2, 2, 64), (4, 2, 128), (16, 2, 128)])
+def test_isolated_tokens_between_trees(Hq, Hkv, D):
+    w = from_sequences(_trees_around_singles(Hq + D, 700), Hq=Hq, Hkv=Hkv, D=D, dtype="bf16",
+                       seed_base=12_000 + Hq + D, row_len=4608)
+    _run_full(w, label=f"isolated_tokens_Hq{Hq}_Hkv{Hkv}_D{D}")
+
+
+def test_padding_slots_attend_to_themselves():
+    """grpo_group at full size (18,447 tokens in a 32,768-slot row) with random values in the padding
+    slots too: a padding slot is isolated (subtree_end[j] = j), so its softmax has one term --
+    out = v, lse = scale q.k, dq = dk = 0 and dv = the sum of its group's dout rows -- and the
+    real slots' results do not depend on what the padding holds."""
+    import torch
+
+    import prefix_tree_packed_dfs_amd as lib
+    w = standard(2)
+    log(f"case padding_slots: {w.name} Hq={w.Hq} Hkv={w.Hkv} D={w.D}")
+    parent, seq_last = lib.tree_build_trie(w.sequences, min_shared=64)
+    n = len(parent)
+    R = w.row_length(n)
+    lay = lib.tree_pack_layout(parent, seq_last, R)
+    se = torch.from_numpy(lay.subtree_end.astype(np.int32)).view(1, R).cuda()
+    g = torch.Generator().manual_seed(5)
+    mk = lambda H: torch.randn(1, R, H, w.D, generator=g).to(torch.bfloat16)  # noqa: E731
+    q, k, v, do = mk(w.Hq), mk(w.Hkv), mk(w.Hkv), mk(w.Hq)
+    res = []
+    for zero_pad in (False, True):
+        t = [x.clone() for x in (q, k, v, do)]
+        if zero_pad:
+            for x in t:
+                x[:, n:] = 0
+        t = [x.cuda() for x in t]
+        out, lse = lib.tree_attn_fwd(t[0], t[1], t[2], se)
+        dq, dk, dv = lib.tree_attn_bwd(t[0], t[1], t[2], se, out, lse, t[3])
+        torch.cuda.synchronize()
+        res.append([x.cpu() for x in (out, lse, dq, dk, dv)])
+    (out, lse, dq, dk, dv), (out0, lse0, dq0, dk0, dv0) = res
+    # real slots: identical whatever the padding holds
+    assert torch.equal(out[:, :n], out0[:, :n]) and torch.equal(lse[:, :, :n], lse0[:, :, :n])
+    assert torch.equal(dq[:, :n], dq0[:, :n])
+    assert torch.equal(dk[:, :n], dk0[:, :n]) and torch.equal(dv[:, :n], dv0[:, :n])
+    # padding slots: the one-key closed form
+    G = w.Hq // w.Hkv
+    qp = q[0, n:].double().numpy()
+    kp = k[0, n:].double().numpy()
+    vp = v[0, n:].double().numpy()
+    dop = do[0, n:].double().numpy()
+    kq = np.repeat(kp, G, axis=1)
+    want_lse = (qp * kq).sum(-1).T * w.D ** -0.5                       # [Hq, pads]
+    got_lse = lse[0, :, n:].double().numpy()
+    assert np.abs(got_lse - want_lse).max() <= 1e-5 * (1 + np.abs(want_lse).max())
+    assert torch.equal(out[0, n:], torch.repeat_interleave(v[0, n:], G, dim=1))
+    # exactly zero where the kernels see a whole block of isolated slots; in the block that mixes
+    # padding with the last packed tokens, zero up to the rounding of dP - delta (fp32)
+    dq_pad, dk_pad = dq[0, n:].abs().max().item(), dk[0, n:].abs().max().item()
+    assert dq_pad <= 1e-3 and dk_pad <= 1e-3, (dq_pad, dk_pad)
+    blk = (n + 255) // 256 * 256
+    assert not dq[0, blk:].any() and not dk[0, blk:].any()
+    want_dv = dop.reshape(R - n, w.Hkv, G, w.D).sum(axis=2)
+    got_dv = dv[0, n:].double().numpy()
+    assert np.all(np.abs(got_dv - want_dv) <= 2.0 ** -8 * np.abs(want_dv) + 1e-6)
+    log(f"    {R - n} padding slots: out = v, lse err {np.abs(got_lse - want_lse).max():.2e}, "
+        f"max |dq| {dq_pad:.1e}, max |dk| {dk_pad:.1e}, dv err {np.abs(got_dv - want_dv).max():.2e}")
