@@ -69,17 +69,29 @@ int num_cus() {
 // ---------------------------------------------------------------------------
 constexpr int kPlanBuckets = 4096;
 
+// Exclusive prefix sum over the 1024 threads of the workgroup: inside each
+// wave by shuffles, then over the 16 wave totals (s_scan holds at least 16 ints).
 __device__ int block_exclusive_scan(int v, int* s_scan) {
-    const int tid = threadIdx.x;
-    s_scan[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int x = tid >= off ? s_scan[tid - off] : 0;
-        __syncthreads();
-        s_scan[tid] += x;
-        __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
     }
-    const int r = s_scan[tid] - v;
+    if (lane == 63) s_scan[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        int t = lane < 16 ? s_scan[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int y = __shfl_up(t, off, 64);
+            if (lane >= off) t += y;
+        }
+        if (lane < 16) s_scan[lane] = t;  // inclusive totals of waves 0..lane
+    }
+    __syncthreads();
+    const int r = x - v + (wave > 0 ? s_scan[wave - 1] : 0);
     __syncthreads();
     return r;
 }
@@ -226,42 +238,64 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
 
 // ---------------------------------------------------------------------------
 // Sum the chunk partials of split tiles in chunk order and write bf16 dK, dV.
-// grid (kSplitSlots / 2 [an upper bound on split tiles x KV heads], 8 chunks
-// of 32 keys), 256 threads.
+// grid (kSplitSlots / 2 [an upper bound on split tiles x KV heads], kKvTile /
+// kReduceKeys), 256 threads; a thread owns kReducePer float4 positions of the
+// workgroup's keys and walks the chunks with their loads in flight together.
+constexpr int kReduceKeys = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce(const int* __restrict__ ctrl,
                                                  const int4* __restrict__ split_tiles,
                                                  const float* __restrict__ partial, int N, int Hkv,
                                                  __bf16* __restrict__ dk, __bf16* __restrict__ dv) {
+    constexpr int ROW4 = D / 4;                          // float4 per key row
+    constexpr int PER = 2 * kReduceKeys * ROW4 / 256;   // float4 positions per thread (dK and dV)
+    constexpr int SLOT = 2 * kKvTile * D;               // floats per slot
     const int w = blockIdx.x;
     const int n_split = ctrl[24];
     if (w >= n_split * Hkv) return;
     const int4 st = split_tiles[w / Hkv];
     const int g = w % Hkv;
     const int b = st.x, j0 = st.y * kKvTile;
-    const int k0 = blockIdx.y * 32;
-    constexpr int SLOT = 2 * kKvTile * D;  // floats per slot
-    for (int e = threadIdx.x; e < 2 * 32 * D / 4; e += 256) {
-        const int which = e / (32 * D / 4);           // 0: dK, 1: dV
-        const int rem = e % (32 * D / 4);
-        const int kl = k0 + rem / (D / 4), d4 = rem % (D / 4);
-        const int j = j0 + kl;
-        if (j >= N) continue;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int kk = 0; kk < st.w; ++kk) {
-            const float4 v = *reinterpret_cast<const float4*>(
-                partial + (int64_t)((st.z + kk) * Hkv + g) * SLOT + which * kKvTile * D + kl * D + d4 * 4);
-            acc.x += v.x;
-            acc.y += v.y;
-            acc.z += v.z;
-            acc.w += v.w;
+    const int k0 = blockIdx.y * kReduceKeys;
+    int off[PER];
+    float4 acc[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = threadIdx.x + 256 * i;
+        const int which = e / (kReduceKeys * ROW4);     // 0: dK, 1: dV
+        const int rem = e % (kReduceKeys * ROW4);
+        off[i] = which * kKvTile * D + (k0 + rem / ROW4) * D + (rem % ROW4) * 4;
+        acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const float* base = partial + (int64_t)(st.z * Hkv + g) * SLOT;
+#pragma unroll 2
+    for (int kk = 0; kk < st.w; ++kk) {
+        const float* src = base + (int64_t)kk * Hkv * SLOT;
+        float4 v[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[i] = *reinterpret_cast<const float4*>(src + off[i]);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            acc[i].x += v[i].x;
+            acc[i].y += v[i].y;
+            acc[i].z += v[i].z;
+            acc[i].w += v[i].w;
         }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = threadIdx.x + 256 * i;
+        const int which = e / (kReduceKeys * ROW4);
+        const int rem = e % (kReduceKeys * ROW4);
+        const int j = j0 + k0 + rem / ROW4;
+        if (j >= N) continue;
         bf16x4 o;
-        o[0] = (__bf16)acc.x;
-        o[1] = (__bf16)acc.y;
-        o[2] = (__bf16)acc.z;
-        o[3] = (__bf16)acc.w;
-        __bf16* dst = (which ? dv : dk) + (((int64_t)b * N + j) * Hkv + g) * D + d4 * 4;
+        o[0] = (__bf16)acc[i].x;
+        o[1] = (__bf16)acc[i].y;
+        o[2] = (__bf16)acc[i].z;
+        o[3] = (__bf16)acc[i].w;
+        __bf16* dst = (which ? dv : dk) + (((int64_t)b * N + j) * Hkv + g) * D + (rem % ROW4) * 4;
         *reinterpret_cast<bf16x4*>(dst) = o;
     }
 }
@@ -825,7 +859,7 @@ hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) 
                        (__bf16*)a.dv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_reduce<D>), dim3(kSplitSlots / 2, kKvTile / 32), dim3(256), 0, st, w.ctrl,
+    hipLaunchKernelGGL((bwd_reduce<D>), dim3(kSplitSlots / 2, kKvTile / kReduceKeys), dim3(256), 0, st, w.ctrl,
                        w.split_tiles, w.partial, a.N, a.Hkv, (__bf16*)a.dk, (__bf16*)a.dv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
