@@ -59,11 +59,10 @@ int num_cus() {
 // prefix visit almost the whole row while keys near the leaves visit a few
 // blocks, so a tile whose range exceeds C blocks is cut at multiples of C
 // (absolute block positions, C = budget / G; the budget doubles until the
-// chunks fit the partial-sum slots).  Units are then queued bucket by bucket
-// of C query blocks: the units that run together on one XCD read the same
-// query blocks, which stay in its L2.  Each KV head has its own queue
-// (g mod NQ, so one XCD keeps one head's data).  The order of units inside
-// a bucket is arbitrary; every unit's result is the same whatever the order.
+// chunks fit the partial-sum slots).  Each KV head has its own queue (g mod
+// NQ, so one XCD keeps one head's data), ordered longest unit first so that
+// the CUs of an XCD run out of work together.  The order of units of equal
+// length is arbitrary; every unit's result is the same whatever the order.
 // ctrl: [0..7] queue counters, [8..15] lengths, [16..23] starts, [24] split tiles.
 // tile_plan[u]: {first block, last block, chunks, first slot or -1}.
 // ---------------------------------------------------------------------------
@@ -107,7 +106,6 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
     const int TT = (N + kKvTile - 1) / kKvTile;  // KV tiles per row
     const int BT = B * TT;
     constexpr int SUB = kKvTile / KT, BPT = kKvTile / 32;  // 64-key tiles, 32-key blocks per KV tile
-    const int NB = (N + 31) / 32;
     const int NQ = Hkv < 8 ? Hkv : 8;
     // a tile of isolated keys gets no units (bwd_isolated writes its gradients)
     for (int u = tid; u < BT; u += 1024) {
@@ -186,16 +184,25 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
             }
         }
     }
-    // bucket of a unit: (row, C-block range of its first block), coarsened to fit kPlanBuckets
-    const int NBK = (NB + C - 1) / C;
+    // queue order: longest units first (the units of a KV head's queue run on
+    // one XCD; taking the long ones first keeps its CUs finishing together).
+    // The bucket of a unit is C minus its number of query blocks.
+    const int64_t NKEY = C + 1;
+    auto ukey = [&](const int4& e, int kk) {
+        int nb = e.y - e.x + 1;
+        if (e.z > 1) {
+            const int k = e.x / C + kk;
+            nb = min(e.y, k * C + C - 1) - max(e.x, k * C) + 1;
+        }
+        return C - nb;
+    };
     int shift = 0;
-    while ((((int64_t)B * NBK - 1) >> shift) >= kPlanBuckets) ++shift;
+    while (((NKEY - 1) >> shift) >= kPlanBuckets) ++shift;
     for (int x = tid; x < kPlanBuckets; x += 1024) s_cnt[x] = 0;
     __syncthreads();
     for (int u = u0; u < u1; ++u) {
         const int4 e = tile_plan[u];
-        const int kb = (u / TT) * NBK + e.x / C;
-        for (int kk = 0; kk < e.z; ++kk) atomicAdd(&s_cnt[(kb + kk) >> shift], 1);
+        for (int kk = 0; kk < e.z; ++kk) atomicAdd(&s_cnt[ukey(e, kk) >> shift], 1);
     }
     __syncthreads();
     {  // exclusive scan of the bucket counts, four per thread
@@ -216,9 +223,8 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
     for (int u = u0; u < u1; ++u) {
         const int4 e = tile_plan[u];
         const int b = u / TT, t = u % TT;
-        const int kb = b * NBK + e.x / C;
         for (int kk = 0; kk < e.z; ++kk) {
-            const int pos = atomicAdd(&s_cnt[(kb + kk) >> shift], 1);
+            const int pos = atomicAdd(&s_cnt[ukey(e, kk) >> shift], 1);
             int v0 = 0, v1 = (e.y - e.x + 1) * G, slot = -1;
             if (e.z > 1) {
                 const int k = e.x / C + kk;
