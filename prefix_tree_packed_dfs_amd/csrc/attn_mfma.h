@@ -9,6 +9,8 @@ namespace treeattn {
 
 // Keys per KV tile and rows per MFMA block.
 constexpr int KT = 64;
+// Work queues of the persistent query-stationary kernels (one per XCD).
+constexpr int kItemQueues = 8;
 
 // Query heads one workgroup serves (all heads sharing a KV head, up to 8).
 inline int heads_per_wg(int G) { return G >= 8 ? 8 : G; }
@@ -22,6 +24,7 @@ struct FwdWorkspace {
     int32_t* tile_min;   // [B, T]
     int32_t* tile_max;   // [B, T]
     int32_t* tile_iso;   // [B, T] 1 if every slot of the tile is isolated (sees and is seen by itself only)
+    int32_t* qctr;       // [kItemQueues] work-queue counters of the persistent forward
 };
 
 // Workspace carved by the backward.
@@ -31,6 +34,7 @@ struct BwdWorkspace {
     int32_t* tile_min;   // [B, T]
     int32_t* tile_max;   // [B, T]
     int32_t* tile_iso;   // [B, T]
+    int32_t* qctr;       // [kItemQueues] work-queue counters of the persistent dQ kernel
     // dK/dV work plan: KV tiles of 256 keys whose query range is long are split
     // into chunks of visits; chunks write fp32 partials that a reduce pass sums
     int32_t* ctrl;       // queue counters / lengths / starts, split-tile count
@@ -48,8 +52,11 @@ constexpr int kVisitBudget = 96;
 
 // Smallest and largest subtree_end of every KT-key tile of each row ([B, T]),
 // and whether every slot of the tile is isolated.
+// (Also zeroes the kItemQueues work-queue counters at qctr.)
 hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, int32_t* tmax, int32_t* tiso,
-                              hipStream_t st);
+                              int32_t* qctr, hipStream_t st);
+// Compute units of the current device (cached per device).
+int mfma_num_cus();
 // Gradient rows of the isolated slots (dq = dk = 0, dv = sum of the group's dout rows).
 hipError_t launch_isolated_bwd(const AttnArgs& a, const int32_t* tiso, hipStream_t st);
 size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D);

@@ -22,6 +22,7 @@
 //   bwd_reduce   sums the partials of split tiles in chunk order.
 // dK/dV and dQ recompute S and dP separately (7 products instead of 5) so
 // that no partial dQ has to be summed across workgroups.
+#include <algorithm>
 #include <climits>
 #include <type_traits>
 
@@ -39,18 +40,6 @@ __device__ __forceinline__ T ld16(const void* p) {
     return *reinterpret_cast<const T*>(p);
 }
 
-// Compute units of the current device (cached per device).
-int num_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
 
 // ---------------------------------------------------------------------------
 // dK/dV work plan (one workgroup).  A KV tile of kKvTile keys visits every
@@ -592,16 +581,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
 // dQ: grid (n_qtiles * B * Hkv * n_chunks), 512 threads; same work split as
 // the forward (BM positions x HB heads per workgroup, 32 rows per wave).
 // ---------------------------------------------------------------------------
+// One work item of dQ: BM positions x HB query heads of one KV head.
 template <int D, int HB>
-__global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                                                 const __bf16* __restrict__ v, const __bf16* __restrict__ out,
-                                                 const __bf16* __restrict__ dout, const float* __restrict__ lse,
-                                                 float* __restrict__ delta, float* __restrict__ lse2,
-                                                 const int32_t* __restrict__ se,
-                                                 const int32_t* __restrict__ tmin, const int32_t* __restrict__ tmax,
-                                                 const int32_t* __restrict__ tiso,
-                                                 int B, int N, int Hq, int Hkv, int T, int n_qtiles, int n_chunks,
-                                                 float scale_log2, float scale, __bf16* __restrict__ dq) {
+__device__ __forceinline__ void dq_item(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                        const __bf16* __restrict__ v, const __bf16* __restrict__ out,
+                                        const __bf16* __restrict__ dout, const float* __restrict__ lse,
+                                        float* __restrict__ delta, float* __restrict__ lse2,
+                                        const int32_t* __restrict__ se, const int32_t* __restrict__ tmin,
+                                        const int32_t* __restrict__ tmax, const int32_t* __restrict__ tiso, int B,
+                                        int N, int Hq, int Hkv, int T, int n_qtiles, int n_chunks, float scale_log2,
+                                        float scale, __bf16* __restrict__ dq, int item, char* smem, int* list,
+                                        int* list_meta) {
     constexpr int BM = 256 / HB;
     constexpr int NC = D / 16, NDB = D / 32;
     constexpr int CPR = D / 8;
@@ -614,16 +604,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
     static_assert(2 * PER_TILE < 16, "wait counts");
     constexpr int LCAP = 1024;
     constexpr int FULL = 1 << 30;
-    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
-    __shared__ int list[LCAP];
-    __shared__ int list_meta[2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: load bases stay scalar
     const int l32 = lane & 31, hi = lane >> 5;
     const int GH = B * Hkv * n_chunks;
-    const int gi = blockIdx.x % GH;
-    const int qi = blockIdx.x / GH;
+    const int gi = item % GH;
+    const int qi = item / GH;
     const int qtile = n_qtiles - 1 - qi;
     const int chunk = gi % n_chunks;
     const int g = (gi / n_chunks) % Hkv;
@@ -827,25 +814,57 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
     }
 }
 
+// Persistent dQ: one 512-thread workgroup per CU takes work items from NQ
+// queues, numbered and assigned as in the persistent forward.
+template <int D, int HB>
+__global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                 const __bf16* __restrict__ v, const __bf16* __restrict__ out,
+                                                 const __bf16* __restrict__ dout, const float* __restrict__ lse,
+                                                 float* __restrict__ delta, float* __restrict__ lse2,
+                                                 const int32_t* __restrict__ se,
+                                                 const int32_t* __restrict__ tmin, const int32_t* __restrict__ tmax,
+                                                 const int32_t* __restrict__ tiso,
+                                                 int B, int N, int Hq, int Hkv, int T, int n_qtiles, int n_chunks,
+                                                 float scale_log2, float scale, __bf16* __restrict__ dq,
+                                                 int* __restrict__ qctr, int NQ, int n_items) {
+    constexpr int STAGE = 2 * KT * D * 2 + KT * 4;
+    __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];
+    __shared__ int list[1024];
+    __shared__ int list_meta[2];
+    __shared__ int s_item;
+    const int qx = blockIdx.x % NQ;
+    for (;;) {
+        if (threadIdx.x == 0) s_item = qx + NQ * atomicAdd(&qctr[qx], 1);
+        __syncthreads();
+        const int item = __builtin_amdgcn_readfirstlane(s_item);
+        __syncthreads();
+        if (item >= n_items) break;
+        dq_item<D, HB>(q, k, v, out, dout, lse, delta, lse2, se, tmin, tmax, tiso, B, N, Hq, Hkv, T, n_qtiles,
+                       n_chunks, scale_log2, scale, dq, item, smem, list, list_meta);
+        __syncthreads();  // the stages and the list are reused by the next item
+    }
+}
+
 template <int D, int HB>
 hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_t st) {
     constexpr int BM = 256 / HB;
     const int G = a.Hq / a.Hkv;
     const int n_chunks = G / HB;
     const int n_qtiles = (a.N + BM - 1) / BM;
-    const int64_t blocks = (int64_t)n_qtiles * a.B * a.Hkv * n_chunks;
-    hipLaunchKernelGGL((bwd_dq<D, HB>), dim3((unsigned)blocks), dim3(512), 0, st, (const __bf16*)a.q,
+    const int64_t items = (int64_t)n_qtiles * a.B * a.Hkv * n_chunks;
+    const int grid = (int)std::min<int64_t>(items, mfma_num_cus());
+    const int NQ = std::min(kItemQueues, grid);
+    hipLaunchKernelGGL((bwd_dq<D, HB>), dim3((unsigned)grid), dim3(512), 0, st, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.out, (const __bf16*)a.dout, a.lse,
-                       w.delta, w.lse2, a.se,
-                       w.tile_min, w.tile_max, w.tile_iso, a.B, a.N, a.Hq, a.Hkv, T, n_qtiles,
-                       n_chunks, a.scale * kLog2e, a.scale, (__bf16*)a.dq);
+                       w.delta, w.lse2, a.se, w.tile_min, w.tile_max, w.tile_iso, a.B, a.N, a.Hq, a.Hkv, T,
+                       n_qtiles, n_chunks, a.scale * kLog2e, a.scale, (__bf16*)a.dq, w.qctr, NQ, (int)items);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
-    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, w.tile_iso, st);
+    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, w.tile_iso, w.qctr, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_plan, dim3(1), dim3(1024), 0, st, w.tile_max, w.tile_iso, a.B, a.N, T, a.Hq / a.Hkv,
                        a.Hkv, w.ctrl, w.tile_plan, w.units, w.split_tiles);
@@ -859,7 +878,7 @@ hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) 
         default: e = launch_dq<D, 8>(a, w, T, st); break;
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv<D>), dim3((unsigned)num_cus()), dim3(512), 0, st, (const __bf16*)a.q,
+    hipLaunchKernelGGL((bwd_dkdv<D>), dim3((unsigned)mfma_num_cus()), dim3(512), 0, st, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, w.lse2, w.delta, a.se, a.N,
                        a.Hq, a.Hkv, a.scale * kLog2e, a.scale, w.ctrl, w.units, w.partial, (__bf16*)a.dk,
                        (__bf16*)a.dv);
@@ -888,7 +907,7 @@ size_t plan_bytes(int B, int N, int Hkv, int D) {
 size_t mfma_bwd_ws_bytes(int B, int N, int Hq, int Hkv, int D) {
     const size_t T = (size_t)(N + KT - 1) / KT;
     return 2 * align256((size_t)B * Hq * N * sizeof(float)) + 3 * align256((size_t)B * T * sizeof(int32_t)) +
-           plan_bytes(B, N, Hkv, D);
+           align256(kItemQueues * sizeof(int32_t)) + plan_bytes(B, N, Hkv, D);
 }
 
 BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D) {
@@ -905,6 +924,8 @@ BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D) {
     p += align256((size_t)B * T * sizeof(int32_t));
     w.tile_iso = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)B * T * sizeof(int32_t));
+    w.qctr = reinterpret_cast<int32_t*>(p);
+    p += align256(kItemQueues * sizeof(int32_t));
     const size_t TT = (size_t)(N + kKvTile - 1) / kKvTile;
     const size_t ucap = (size_t)kSplitSlots + (size_t)B * TT * Hkv;
     w.ctrl = reinterpret_cast<int32_t*>(p);

@@ -26,6 +26,7 @@
 // (ds_read_b64_tr_b16) that also put the keys of each 16-key group in the
 // order the accumulator holds them.  Online softmax in fp32 with exp2 and a
 // log2(e)-prescaled scale; P is rounded to bf16 for the PV product.
+#include <algorithm>
 #include <climits>
 
 #include "attn_mfma.h"
@@ -42,8 +43,9 @@ constexpr float kLn2 = 0.69314718055994531f;
 // B), 256 threads, one wave per tile.
 __global__ __launch_bounds__(256) void fwd_prep(const int32_t* __restrict__ se, int N, int T,
                                                 int32_t* __restrict__ tmin, int32_t* __restrict__ tmax,
-                                                int32_t* __restrict__ tiso) {
+                                                int32_t* __restrict__ tiso, int32_t* __restrict__ qctr) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6), b = blockIdx.y, lane = threadIdx.x & 63;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kItemQueues) qctr[threadIdx.x] = 0;  // work queues
     if (t >= T) return;
     const int j = t * KT + lane;
     const int s = j < N ? se[(int64_t)b * N + j] : -1;
@@ -184,14 +186,14 @@ __global__ __launch_bounds__(256) void bwd_isolated(const __bf16* __restrict__ d
     }
 }
 
+// One work item of the forward: BM positions x HB query heads of one KV head.
 template <int D, int HB>
-__global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                                                   const __bf16* __restrict__ v, const int32_t* __restrict__ se,
-                                                   const int32_t* __restrict__ tmin,
-                                                   const int32_t* __restrict__ tmax,
-                                                   const int32_t* __restrict__ tiso, int B, int N, int Hq,
-                                                   int Hkv, int T, int n_qtiles, int n_chunks, float scale_log2,
-                                                   __bf16* __restrict__ out, float* __restrict__ lse) {
+__device__ __forceinline__ void fwd_item(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                         const __bf16* __restrict__ v, const int32_t* __restrict__ se,
+                                         const int32_t* __restrict__ tmin, const int32_t* __restrict__ tmax,
+                                         const int32_t* __restrict__ tiso, int B, int N, int Hq, int Hkv, int T,
+                                         int n_qtiles, int n_chunks, float scale_log2, __bf16* __restrict__ out,
+                                         float* __restrict__ lse, int item, char* smem, int* list, int* list_meta) {
     constexpr int BM = 256 / HB;          // positions per workgroup (8 waves x 32 rows = BM x HB)
     constexpr int NC = D / 16;            // 16-wide chunks of the head dim
     constexpr int NDB = D / 32;           // 32-row blocks of the head dim
@@ -204,16 +206,13 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
     constexpr int PER_TILE = 2 * KDMA + 1;    // vector memory ops per wave per tile
     constexpr int LCAP = 1024;                // visible tiles listed per pass
     constexpr int FULL = 1 << 30;
-    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
-    __shared__ int list[LCAP];
-    __shared__ int list_meta[2];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: load bases stay scalar
     const int l32 = lane & 31, hi = lane >> 5;
     const int GH = B * Hkv * n_chunks;
-    const int gi = blockIdx.x % GH;
-    const int qi = blockIdx.x / GH;
+    const int gi = item % GH;
+    const int qi = item / GH;
     const int qt = n_qtiles - 1 - qi;  // deeper (later) query tiles first
     const int chunk = gi % n_chunks;
     const int g = (gi / n_chunks) % Hkv;
@@ -446,25 +445,59 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
     }
 }
 
+// Persistent forward: one 512-thread workgroup per CU takes work items from
+// NQ queues (workgroup w serves queue w mod NQ; queue x holds items x, x + NQ,
+// ...).  Items are numbered deepest query block first, with the KV head
+// fastest, so the longest items go first and a queue keeps to one KV head
+// whenever the heads are a multiple of NQ (its K and V stay in one XCD's L2).
+template <int D, int HB>
+__global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                   const __bf16* __restrict__ v, const int32_t* __restrict__ se,
+                                                   const int32_t* __restrict__ tmin,
+                                                   const int32_t* __restrict__ tmax,
+                                                   const int32_t* __restrict__ tiso, int B, int N, int Hq,
+                                                   int Hkv, int T, int n_qtiles, int n_chunks, float scale_log2,
+                                                   __bf16* __restrict__ out, float* __restrict__ lse,
+                                                   int* __restrict__ qctr, int NQ, int n_items) {
+    constexpr int STAGE = 2 * KT * D * 2 + KT * 4;
+    __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];
+    __shared__ int list[1024];
+    __shared__ int list_meta[2];
+    __shared__ int s_item;
+    const int qx = blockIdx.x % NQ;
+    for (;;) {
+        if (threadIdx.x == 0) s_item = qx + NQ * atomicAdd(&qctr[qx], 1);
+        __syncthreads();
+        const int item = __builtin_amdgcn_readfirstlane(s_item);
+        __syncthreads();
+        if (item >= n_items) break;
+        fwd_item<D, HB>(q, k, v, se, tmin, tmax, tiso, B, N, Hq, Hkv, T, n_qtiles, n_chunks, scale_log2, out, lse,
+                        item, smem, list, list_meta);
+        __syncthreads();  // the stages and the list are reused by the next item
+    }
+}
+
 template <int D, int HB>
 hipError_t launch_main(const AttnArgs& a, const FwdWorkspace& w, int T, hipStream_t st) {
     constexpr int BM = 256 / HB;
     const int G = a.Hq / a.Hkv;
     const int n_chunks = G / HB;
     const int n_qtiles = (a.N + BM - 1) / BM;
-    const int64_t blocks = (int64_t)n_qtiles * a.B * a.Hkv * n_chunks;
+    const int64_t items = (int64_t)n_qtiles * a.B * a.Hkv * n_chunks;
+    const int grid = (int)std::min<int64_t>(items, mfma_num_cus());
+    const int NQ = std::min(kItemQueues, grid);
     const float scale_log2 = a.scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((fwd_main<D, HB>), dim3((unsigned)blocks), dim3(512), 0, st, (const __bf16*)a.q,
+    hipLaunchKernelGGL((fwd_main<D, HB>), dim3((unsigned)grid), dim3(512), 0, st, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, a.se, w.tile_min, w.tile_max, w.tile_iso, a.B,
-                       a.N, a.Hq,
-                       a.Hkv, T, n_qtiles, n_chunks, scale_log2, (__bf16*)a.out, a.lse);
+                       a.N, a.Hq, a.Hkv, T, n_qtiles, n_chunks, scale_log2, (__bf16*)a.out, a.lse, w.qctr, NQ,
+                       (int)items);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
-    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, w.tile_iso, st);
+    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, w.tile_iso, w.qctr, st);
     if (e != hipSuccess) return e;
     switch (heads_per_wg(a.Hq / a.Hkv)) {
         case 1: e = launch_main<D, 1>(a, w, T, st); break;
@@ -488,7 +521,7 @@ size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D) {
     (void)Hkv;
     (void)D;
     const size_t T = (size_t)(N + KT - 1) / KT;
-    return 3 * align256((size_t)B * T * sizeof(int32_t));
+    return 3 * align256((size_t)B * T * sizeof(int32_t)) + align256(kItemQueues * sizeof(int32_t));
 }
 
 FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D) {
@@ -502,13 +535,15 @@ FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D) {
     w.tile_max = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)B * T * sizeof(int32_t));
     w.tile_iso = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)B * T * sizeof(int32_t));
+    w.qctr = reinterpret_cast<int32_t*>(p);
     return w;
 }
 
 hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, int32_t* tmax, int32_t* tiso,
-                              hipStream_t st) {
+                              int32_t* qctr, hipStream_t st) {
     const int T = (N + KT - 1) / KT;
-    hipLaunchKernelGGL(fwd_prep, dim3((T + 3) / 4, B), dim3(256), 0, st, se, N, T, tmin, tmax, tiso);
+    hipLaunchKernelGGL(fwd_prep, dim3((T + 3) / 4, B), dim3(256), 0, st, se, N, T, tmin, tmax, tiso, qctr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(iso_scan, dim3(B), dim3(1024), 0, st, tmax, T, tiso);
@@ -526,6 +561,18 @@ hipError_t launch_isolated_bwd(const AttnArgs& a, const int32_t* tiso, hipStream
                            (const __bf16*)a.dout, tiso, a.N, a.Hq, a.Hkv, T, (__bf16*)a.dq, (__bf16*)a.dk,
                            (__bf16*)a.dv);
     return hipGetLastError();
+}
+
+int mfma_num_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 hipError_t mfma_attn_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st) {
