@@ -6,20 +6,22 @@
 //   dV = P^T dout,   dP = dout V^T,   dS = P * (dP - delta),
 //   dK = scale dS^T Q,   dQ = scale dS K.
 // Kernels, in launch order, no atomics on results (bitwise reproducible):
-//   tile ranges  min / max subtree_end per 64-key tile (shared with the
-//                forward);
+//   tile ranges  min / max subtree_end per 64-key tile and which tiles hold
+//                isolated slots only (shared with the forward);
 //   bwd_plan     the dK/dV work plan (split long KV tiles, per-XCD queues);
-//   bwd_dq       query-stationary, shaped like the forward: S^T = K Q^T and
-//                dP^T = V dout^T with Q, dout in registers, then
-//                dQ^T += K^T dS^T with dS^T taken from the accumulator; it
-//                also writes delta and lse * log2(e) for the next kernel;
+//   bwd_dq       query-stationary and persistent, shaped like the forward:
+//                S^T = K Q^T and dP^T = V dout^T with Q, dout in registers,
+//                then dQ^T += K^T dS^T with dS^T taken from the accumulator;
+//                it also writes delta and lse * log2(e) for the next kernel;
 //   bwd_dkdv     KV-stationary and persistent: a workgroup owns 256 keys of
 //                one KV head (32 per wave) and walks the query blocks its
 //                keys can see, for every query head of the group:
 //                  S = Q K^T, dP = dout V^T     (A = Q, dout rows from LDS)
 //                  dV^T += dout^T P, dK^T += Q^T dS   (A by transposed LDS
 //                  loads, B = P, dS straight from the S / dP accumulators)
-//   bwd_reduce   sums the partials of split tiles in chunk order.
+//   bwd_reduce   sums the partials of split tiles in chunk order;
+//   bwd_isolated the one-key gradients of isolated slots (dq = dk = 0,
+//                dv = the group's dout rows summed).
 // dK/dV and dQ recompute S and dP separately (7 products instead of 5) so
 // that no partial dQ has to be summed across workgroups.
 #include <algorithm>

@@ -9,12 +9,16 @@
 // which is the pages' decomposition into fully visible ancestor blocks, a
 // causal block on the query's own segment, and skipped blocks.
 //
-// Work decomposition (one workgroup = 4 waves = 256 query rows):
+// Work decomposition (one work item = 8 waves = 256 query rows):
 //   * the rows are BM positions x HB query heads that share one KV head
 //     (BM * HB = 256), so a K/V tile staged once in LDS serves every head of
 //     the GQA group;
-//   * each wave owns two 32-row query blocks and keeps their Q fragments in
-//     registers; every K or V fragment read from LDS feeds two MFMAs.
+//   * each wave owns one 32-row query block (32 positions of one head) and
+//     keeps its Q fragments in registers;
+//   * the kernel is persistent: one workgroup per CU takes items from
+//     per-XCD queues, deepest query block first.
+// Slots that see and are seen only by themselves (padding, one-token
+// sequences) are left to fwd_isolated, which writes their one-key result.
 // Products are v_mfma_f32_32x32x16_bf16 in the transposed orientation:
 //   S^T = K Q^T   (A = K from LDS, B = Q^T from registers)
 //   O^T += V^T P^T (A = V^T from LDS, B = P^T straight from the S^T accumulator)
