@@ -235,9 +235,10 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
 
 // ---------------------------------------------------------------------------
 // Sum the chunk partials of split tiles in chunk order and write bf16 dK, dV.
-// grid (kSplitSlots / 2 [an upper bound on split tiles x KV heads], kKvTile /
-// kReduceKeys), 256 threads; a thread owns kReducePer float4 positions of the
-// workgroup's keys and walks the chunks with their loads in flight together.
+// The work is (split tile, KV head, group of kReduceKeys keys); the grid
+// strides over it (the number of split tiles is known only on the device).  A
+// thread owns a few float4 positions of its group and walks the chunks with
+// their loads in flight together.
 constexpr int kReduceKeys = 16;
 
 template <int D>
@@ -248,13 +249,14 @@ __global__ __launch_bounds__(256) void bwd_reduce(const int* __restrict__ ctrl,
     constexpr int ROW4 = D / 4;                          // float4 per key row
     constexpr int PER = 2 * kReduceKeys * ROW4 / 256;   // float4 positions per thread (dK and dV)
     constexpr int SLOT = 2 * kKvTile * D;               // floats per slot
-    const int w = blockIdx.x;
     const int n_split = ctrl[24];
-    if (w >= n_split * Hkv) return;
+    constexpr int KG = kKvTile / kReduceKeys;  // key groups per tile
+    for (int wk = blockIdx.x; wk < n_split * Hkv * KG; wk += gridDim.x) {
+    const int w = wk / KG;
     const int4 st = split_tiles[w / Hkv];
     const int g = w % Hkv;
     const int b = st.x, j0 = st.y * kKvTile;
-    const int k0 = blockIdx.y * kReduceKeys;
+    const int k0 = (wk % KG) * kReduceKeys;
     int off[PER];
     float4 acc[PER];
 #pragma unroll
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(256) void bwd_reduce(const int* __restrict__ ctrl,
         acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const float* base = partial + (int64_t)(st.z * Hkv + g) * SLOT;
-#pragma unroll 2
+#pragma unroll 4
     for (int kk = 0; kk < st.w; ++kk) {
         const float* src = base + (int64_t)kk * Hkv * SLOT;
         float4 v[PER];
@@ -294,6 +296,7 @@ __global__ __launch_bounds__(256) void bwd_reduce(const int* __restrict__ ctrl,
         o[3] = (__bf16)acc[i].w;
         __bf16* dst = (which ? dv : dk) + (((int64_t)b * N + j) * Hkv + g) * D + (rem % ROW4) * 4;
         *reinterpret_cast<bf16x4*>(dst) = o;
+    }
     }
 }
 
@@ -886,7 +889,7 @@ hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) 
                        (__bf16*)a.dv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_reduce<D>), dim3(kSplitSlots / 2, kKvTile / kReduceKeys), dim3(256), 0, st, w.ctrl,
+    hipLaunchKernelGGL((bwd_reduce<D>), dim3(4 * mfma_num_cus()), dim3(256), 0, st, w.ctrl,
                        w.split_tiles, w.partial, a.N, a.Hkv, (__bf16*)a.dk, (__bf16*)a.dv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -117,14 +117,17 @@ constexpr int kIsoSplit = 8;
 template <int D>
 __global__ __launch_bounds__(256) void fwd_isolated(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                     const __bf16* __restrict__ v, const int32_t* __restrict__ tiso,
-                                                    int N, int Hq, int Hkv, int T, float scale,
+                                                    int B, int N, int Hq, int Hkv, int T, float scale,
                                                     __bf16* __restrict__ out, float* __restrict__ lse) {
-    const int t = blockIdx.x, b = blockIdx.z;
-    if (!tiso[(int64_t)b * T + t]) return;
     constexpr int LPR = D / 8, RPW = 64 / LPR;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int G = Hq / Hkv, rows = KT * Hq / kIsoSplit, rbase = blockIdx.y * rows;
+    const int G = Hq / Hkv, rows = KT * Hq / kIsoSplit;
     const int e = (lane % LPR) * 8;
+    // work (row, tile, part of the tile); the grid strides over it
+    for (int64_t wk = blockIdx.x; wk < (int64_t)B * T * kIsoSplit; wk += gridDim.x) {
+    const int t = (int)(wk / kIsoSplit % T), b = (int)(wk / kIsoSplit / T);
+    if (!tiso[(int64_t)b * T + t]) continue;
+    const int rbase = (int)(wk % kIsoSplit) * rows;
 #pragma unroll 4
     for (int r0 = rbase + wave * RPW; r0 < rbase + rows; r0 += 4 * RPW) {
         const int r = r0 + lane / LPR;
@@ -144,6 +147,7 @@ __global__ __launch_bounds__(256) void fwd_isolated(const __bf16* __restrict__ q
             if (lane % LPR == 0) lse[((int64_t)b * Hq + h) * N + slot] = dot * scale;
         }
     }
+    }
 }
 
 // Isolated slots of the backward: P = 1 on the diagonal and nothing else, so
@@ -151,24 +155,26 @@ __global__ __launch_bounds__(256) void fwd_isolated(const __bf16* __restrict__ q
 // the dout rows of the query heads sharing the key's head.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_isolated(const __bf16* __restrict__ dout,
-                                                    const int32_t* __restrict__ tiso, int N, int Hq, int Hkv,
+                                                    const int32_t* __restrict__ tiso, int B, int N, int Hq, int Hkv,
                                                     int T, __bf16* __restrict__ dq, __bf16* __restrict__ dk,
                                                     __bf16* __restrict__ dv) {
-    const int t = blockIdx.x, b = blockIdx.z;
-    if (!tiso[(int64_t)b * T + t]) return;
     constexpr int LPR = D / 8, RPW = 64 / LPR;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int G = Hq / Hkv;
     const int e = (lane % LPR) * 8;
     const bf16x8 z = {};
-    const int qrows = KT * Hq / kIsoSplit, qbase = blockIdx.y * qrows;
+    for (int64_t wk = blockIdx.x; wk < (int64_t)B * T * kIsoSplit; wk += gridDim.x) {
+    const int t = (int)(wk / kIsoSplit % T), b = (int)(wk / kIsoSplit / T);
+    if (!tiso[(int64_t)b * T + t]) continue;
+    const int part = (int)(wk % kIsoSplit);
+    const int qrows = KT * Hq / kIsoSplit, qbase = part * qrows;
 #pragma unroll 4
     for (int r0 = qbase + wave * RPW; r0 < qbase + qrows; r0 += 4 * RPW) {  // dq rows
         const int r = r0 + lane / LPR;
         const int slot = t * KT + r / Hq;
         if (slot < N) *reinterpret_cast<bf16x8*>(dq + (((int64_t)b * N + slot) * Hq + r % Hq) * D + e) = z;
     }
-    const int kvrows = KT * Hkv / kIsoSplit, kvbase = blockIdx.y * kvrows;
+    const int kvrows = KT * Hkv / kIsoSplit, kvbase = part * kvrows;
 #pragma unroll 4
     for (int r0 = kvbase + wave * RPW; r0 < kvbase + kvrows; r0 += 4 * RPW) {  // dk, dv rows
         const int r = r0 + lane / LPR;
@@ -187,6 +193,7 @@ __global__ __launch_bounds__(256) void bwd_isolated(const __bf16* __restrict__ d
         const int64_t kv = (((int64_t)b * N + slot) * Hkv + g) * D + e;
         *reinterpret_cast<bf16x8*>(dk + kv) = z;
         *reinterpret_cast<bf16x8*>(dv + kv) = o;
+    }
     }
 }
 
@@ -481,6 +488,12 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
     }
 }
 
+// Workgroups of the isolated-slot kernels: enough to keep every CU streaming,
+// never more than there is work (B * T tiles x kIsoSplit parts).
+unsigned iso_grid(int B, int T) {
+    return (unsigned)std::min<int64_t>((int64_t)B * T * kIsoSplit, 8 * (int64_t)mfma_num_cus());
+}
+
 template <int D, int HB>
 hipError_t launch_main(const AttnArgs& a, const FwdWorkspace& w, int T, hipStream_t st) {
     constexpr int BM = 256 / HB;
@@ -510,9 +523,8 @@ hipError_t launch_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st) 
         default: e = launch_main<D, 8>(a, w, T, st); break;
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fwd_isolated<D>), dim3((unsigned)T, kIsoSplit, (unsigned)a.B), dim3(256), 0, st,
-                       (const __bf16*)a.q,
-                       (const __bf16*)a.k, (const __bf16*)a.v, w.tile_iso, a.N, a.Hq, a.Hkv, T, a.scale,
+    hipLaunchKernelGGL((fwd_isolated<D>), dim3(iso_grid(a.B, T)), dim3(256), 0, st, (const __bf16*)a.q,
+                       (const __bf16*)a.k, (const __bf16*)a.v, w.tile_iso, a.B, a.N, a.Hq, a.Hkv, T, a.scale,
                        (__bf16*)a.out, a.lse);
     return hipGetLastError();
 }
@@ -557,13 +569,11 @@ hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, in
 hipError_t launch_isolated_bwd(const AttnArgs& a, const int32_t* tiso, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
     if (a.D == 64)
-        hipLaunchKernelGGL((bwd_isolated<64>), dim3((unsigned)T, kIsoSplit, (unsigned)a.B), dim3(256), 0, st,
-                           (const __bf16*)a.dout, tiso, a.N, a.Hq, a.Hkv, T, (__bf16*)a.dq, (__bf16*)a.dk,
-                           (__bf16*)a.dv);
+        hipLaunchKernelGGL((bwd_isolated<64>), dim3(iso_grid(a.B, T)), dim3(256), 0, st, (const __bf16*)a.dout,
+                           tiso, a.B, a.N, a.Hq, a.Hkv, T, (__bf16*)a.dq, (__bf16*)a.dk, (__bf16*)a.dv);
     else
-        hipLaunchKernelGGL((bwd_isolated<128>), dim3((unsigned)T, kIsoSplit, (unsigned)a.B), dim3(256), 0, st,
-                           (const __bf16*)a.dout, tiso, a.N, a.Hq, a.Hkv, T, (__bf16*)a.dq, (__bf16*)a.dk,
-                           (__bf16*)a.dv);
+        hipLaunchKernelGGL((bwd_isolated<128>), dim3(iso_grid(a.B, T)), dim3(256), 0, st, (const __bf16*)a.dout,
+                           tiso, a.B, a.N, a.Hq, a.Hkv, T, (__bf16*)a.dq, (__bf16*)a.dk, (__bf16*)a.dv);
     return hipGetLastError();
 }
 

@@ -6,8 +6,9 @@
 // by pos * theta^(-2i/D).
 //
 // HBM-bound: every element is read once and written once.  A thread owns four
-// consecutive frequencies of one slot and walks over the heads, so its sines
-// and cosines are computed once and reused H times.  They are computed in fp64
+// (fp32) or eight (bf16: 16-byte accesses) consecutive frequencies of one slot
+// and walks over the heads, so its sines and cosines are computed once and
+// reused H times.  They are computed in fp64
 // (the angle reaches tens of thousands of radians at depth 36K, where an fp32
 // angle would already be off by ~1e-3) and rounded once to the storage type.
 // A slot at depth 0 (a root, or a padding slot) turns by angle 0, which is the
@@ -23,18 +24,18 @@ template <int D>
 __global__ __launch_bounds__(256) void rope_kernel_bf16(__bf16* __restrict__ x, const int32_t* __restrict__ pos,
                                                    int64_t BN, int H, double log2_theta) {
     constexpr int HALF = D / 2;
-    constexpr int QUADS = HALF / 4;  // threads per slot
+    constexpr int OCTS = HALF / 8;  // threads per slot: eight frequencies each
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t slot = gid / QUADS;
-    const int quad = (int)(gid % QUADS);
+    const int64_t slot = gid / OCTS;
+    const int oct = (int)(gid % OCTS);
     if (slot >= BN) return;
     const int p_i = pos[slot];
     if (p_i == 0) return;  // identity
     const double p = (double)p_i;
-    float c[4], s[4];
+    float c[8], s[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int i = quad * 4 + u;
+    for (int u = 0; u < 8; ++u) {
+        const int i = oct * 8 + u;
         // theta^(-2i/D) = 2^(-(2i/D) log2 theta)
         const double ang = p * exp2(-(double)(2 * i) / (double)D * log2_theta);
         double sd, cd;
@@ -44,10 +45,10 @@ __global__ __launch_bounds__(256) void rope_kernel_bf16(__bf16* __restrict__ x, 
     }
     // fp32 products are enough for bf16 storage: one rounding of an fp32
     // expression whose error is far below half a bf16 ulp.
-    __bf16* row = x + slot * (int64_t)H * D + quad * 4;
-    auto rotate = [&](const bf16x4& va, const bf16x4& vb, bf16x4& ra, bf16x4& rb) {
+    __bf16* row = x + slot * (int64_t)H * D + oct * 8;
+    auto rotate = [&](const bf16x8& va, const bf16x8& vb, bf16x8& ra, bf16x8& rb) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             const float xa = (float)va[u], xb = (float)vb[u];
             ra[u] = (__bf16)(xa * c[u] - xb * s[u]);
             rb[u] = (__bf16)(xb * c[u] + xa * s[u]);
@@ -56,24 +57,24 @@ __global__ __launch_bounds__(256) void rope_kernel_bf16(__bf16* __restrict__ x, 
     // heads in groups of four: all loads of a group are in flight together
     int h = 0;
     for (; h + 4 <= H; h += 4) {
-        bf16x4 va[4], vb[4];
+        bf16x8 va[4], vb[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            va[e] = *reinterpret_cast<const bf16x4*>(row + (int64_t)(h + e) * D);
-            vb[e] = *reinterpret_cast<const bf16x4*>(row + (int64_t)(h + e) * D + HALF);
+            va[e] = *reinterpret_cast<const bf16x8*>(row + (int64_t)(h + e) * D);
+            vb[e] = *reinterpret_cast<const bf16x8*>(row + (int64_t)(h + e) * D + HALF);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            bf16x4 ra, rb;
+            bf16x8 ra, rb;
             rotate(va[e], vb[e], ra, rb);
-            *reinterpret_cast<bf16x4*>(row + (int64_t)(h + e) * D) = ra;
-            *reinterpret_cast<bf16x4*>(row + (int64_t)(h + e) * D + HALF) = rb;
+            *reinterpret_cast<bf16x8*>(row + (int64_t)(h + e) * D) = ra;
+            *reinterpret_cast<bf16x8*>(row + (int64_t)(h + e) * D + HALF) = rb;
         }
     }
     for (; h < H; ++h) {
-        bf16x4* a = reinterpret_cast<bf16x4*>(row + (int64_t)h * D);
-        bf16x4* b = reinterpret_cast<bf16x4*>(row + (int64_t)h * D + HALF);
-        bf16x4 ra, rb;
+        bf16x8* a = reinterpret_cast<bf16x8*>(row + (int64_t)h * D);
+        bf16x8* b = reinterpret_cast<bf16x8*>(row + (int64_t)h * D + HALF);
+        bf16x8 ra, rb;
         rotate(*a, *b, ra, rb);
         *a = ra;
         *b = rb;
@@ -135,7 +136,7 @@ extern "C" tree_status tree_rope(tree_dtype dt, void* x, int64_t B, int64_t N, i
     if (!x || !pos_ids) return fail(TREE_ERR_INVALID_ARG, "null pointer argument");
     if (H > (1 << 20)) return fail(TREE_ERR_INVALID_ARG, "too many heads");
     hipStream_t st = (hipStream_t)stream;
-    const int64_t threads = BN * (D / 8);
+    const int64_t threads = BN * (dt == TREE_F32 ? D / 8 : D / 16);
     const int64_t blocks = (threads + 255) / 256;
     if (blocks > 0x7fffffffLL) return fail(TREE_ERR_INVALID_ARG, "row too long");
     const double l2t = std::log2((double)theta);
