@@ -217,6 +217,9 @@ tree_status tree_rope(tree_dtype dt, void* x, int64_t B, int64_t N, int64_t H, i
 /*
  * tree_attn_workspace_bytes - device workspace tree_attn_fwd (bwd = 0) or
  * tree_attn_bwd (bwd = 1) needs for these sizes.  Returns 0 on bad sizes.
+ * The workspace holds per-call tables and work-queue counters that each call
+ * re-initialises on its stream: calls that may run at the same time on the
+ * GPU need workspaces of their own.
  */
 size_t tree_attn_workspace_bytes(tree_dtype dt, int64_t B, int64_t N, int64_t Hq, int64_t Hkv,
                                  int64_t D, int bwd);
@@ -240,7 +243,8 @@ size_t tree_attn_workspace_bytes(tree_dtype dt, int64_t B, int64_t N, int64_t Hq
  *   lse          out [B, Hq, N] fp32
  *   ws, ws_bytes device workspace of at least tree_attn_workspace_bytes(dt, ..., 0) bytes
  *
- * Padding slots (subtree_end[j] == j, no descendants) attend to themselves only.
+ * Padding slots (subtree_end[j] == j, no descendants) attend to themselves only:
+ * out = v, lse = softmax_scale * q . k.
  */
 tree_status tree_attn_fwd(tree_dtype dt, const void* q, const void* k, const void* v,
                           const int32_t* subtree_end, int64_t B, int64_t N, int64_t Hq,
