@@ -254,9 +254,6 @@ __device__ __forceinline__ void fwd_item(const __bf16* __restrict__ q, const __b
             qf[c] = ip < N ? *reinterpret_cast<const bf16x8*>(src + 16 * c) : z;
         }
     }
-    // Q completes before any prefetch is issued: the compiler's wait for it
-    // then does not drain the first tiles' prefetches
-    wait_vmcnt<0>();
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) zero(acc[db]);
@@ -331,6 +328,10 @@ __device__ __forceinline__ void fwd_item(const __bf16* __restrict__ q, const __b
         __syncthreads();
         const int cnt = list_meta[0];
         resume = list_meta[1];
+        // Q (loaded while the list was built) completes before any prefetch is
+        // issued: the compiler's wait for it then does not drain the first
+        // tiles' prefetches
+        wait_vmcnt<0>();
 
         // Software pipeline: S for tile it+1 is issued next to the softmax and
         // PV product of tile it, so the matrix core has work while the VALU
