@@ -100,10 +100,11 @@ def test_random_tree_bf16_no_rope_and_rope(rope):
     _run_full(w, rope=rope, label=f"random_tree_bf16_rope={rope}")
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(2, 2, 64), (4, 1, 64), (8, 1, 128), (16, 2, 128), (3, 3, 128)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(2, 2, 64), (4, 1, 64), (8, 1, 128), (16, 2, 128), (32, 2, 64), (3, 3, 128)])
 def test_random_tree_bf16_head_shapes(Hq, Hkv, D):
-    """Every GQA grouping the matrix-core kernels specialise (1, 4, 8 heads per KV head), head dim 64,
-    and a ratio they do not cover (3 KV heads of 1), which runs on the vector path."""
+    """Every GQA grouping the matrix-core kernels specialise (1, 4, 8 heads per KV head, and 16 as two
+    workgroups of 8), head dim 64, and a ratio they do not cover (3 KV heads of 1), which runs on the
+    vector path."""
     w = _random_workload(700 + Hq * 10 + D, "bf16", Hq=Hq, Hkv=Hkv, D=D, n_seqs=7, max_len=400)
     _run_full(w, label=f"random_tree_bf16_Hq{Hq}_Hkv{Hkv}_D{D}")
 
@@ -190,6 +191,14 @@ def _dout_sum(w, tables, lres):
     _, dkey_slot = slot_rows(w, lres.layout, lres.n)
     do = tables["do"][dkey_slot[:lres.n]].astype(np.float64)
     return do.reshape(lres.n, w.Hkv, w.Hq // w.Hkv, w.D).sum(axis=(0, 2))
+
+
+def test_long_chain_beyond_one_tile_list_sampled():
+    """One 70,000-token sequence: the query blocks near its end see more than 1,024 key tiles, so the
+    visible-tile list is built in several passes, and every key tile's query range is split for dK/dV."""
+    w = from_sequences([np.arange(70_000, dtype=np.int32)], Hq=2, Hkv=1, D=64, dtype="bf16", seed_base=15_000,
+                       row_len=70_016)
+    _run_sampled(w, "long_chain_70000")
 
 
 def test_full_c3_agentic_sampled():
