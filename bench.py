@@ -533,6 +533,29 @@ def main():
     fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
 
+    # one cold step at a time: a 1 GiB write between steps evicts the 256 MB
+    # last-level cache, so the step reads its inputs from HBM
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for i in range(3):
+        flush.fill_(float(i))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(args.warmup + args.steps + i, ev)
+        torch.cuda.synchronize()
+        cold.append(ev[0].elapsed_time(ev[3]))
+    del flush
+    # the matrix-core rate this GPU sustains on a plain chain of bf16 products
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    blocks = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+    lib.tree_mfma_peak(blocks, 256, sink)
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record()
+    peak_flops = lib.tree_mfma_peak(blocks, 20000, sink)
+    p1.record()
+    torch.cuda.synchronize()
+    measured_peak = peak_flops / (p0.elapsed_time(p1) * 1e-3) / 1e12
+
     value = total_flops / (ms_step * 1e-3) / 1e12
     bwd_tf = bwd_flops / (bwd_ms * 1e-3) / 1e12
     rec = {
@@ -556,6 +579,9 @@ def main():
         "tflops_fwd": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 3),
         "tflops_bwd": round(bwd_tf, 3),
         "frac_of_bf16_peak_step": round(value / PEAK_BF16_TFLOPS, 4),
+        "measured_mfma_peak_tflops": round(measured_peak, 1),
+        "frac_of_measured_peak_step": round(value / measured_peak, 4),
+        "cold_ms_per_step": round(float(np.median(cold)), 4),
         "roofline": {
             "kernel": "tree_attn_bwd (every kernel of the call)",
             "bound": "mfma",

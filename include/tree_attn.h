@@ -353,6 +353,19 @@ tree_status tree_gdn_fwd(tree_dtype dt, const void* x, const float* conv_w, int6
                          int64_t n_depths, int64_t n_states, int64_t n, int64_t Hk, int64_t Hv, int64_t dk,
                          int64_t dv, void* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * tree_mfma_peak - measurement aid, not part of the path (device, async).
+ *
+ * Launches `blocks` workgroups of four waves; every wave issues `iters` x 4
+ * bf16 32x32x16 matrix products on register operands (four independent
+ * accumulators), nothing else.  Timing the call on `stream` gives the
+ * matrix-core rate the GPU sustains; the products performed are written to
+ * *flops (host) before the launch.  `sink` is a device buffer of at least 256
+ * floats that the kernel may write (it never does for these operands; the
+ * store only keeps the products live).
+ */
+tree_status tree_mfma_peak(int64_t blocks, int64_t iters, float* sink, double* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

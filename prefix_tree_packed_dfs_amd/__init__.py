@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     tree_gdn_fwd,
     tree_gdn_plan,
     tree_gdn_workspace_bytes,
+    tree_mfma_peak,
     tree_place_leaves,
     tree_pack_layout,
     tree_rope,

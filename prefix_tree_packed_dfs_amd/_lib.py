@@ -83,9 +83,13 @@ lib.tree_gdn_fwd.argtypes = [C.c_int, _vp, _vp, C.c_int64, _vp, _vp, _vp, _vp, C
                              C.c_int64, C.c_int64, C.c_int64, C.c_int64, C.c_int64, C.c_int64, C.c_int64, _vp, _vp,
                              C.c_size_t, _vp]
 
+lib.tree_mfma_peak.restype = C.c_int
+lib.tree_mfma_peak.argtypes = [C.c_int64, C.c_int64, _vp, C.POINTER(C.c_double), _vp]
+
 EXPORTED = ("tree_abi_version", "tree_status_string", "tree_last_error", "tree_build_trie",
             "tree_place_leaves", "tree_pack_layout", "tree_validate_subtree_end", "tree_rope", "tree_attn_workspace_bytes",
-            "tree_attn_fwd", "tree_attn_bwd", "tree_gdn_plan", "tree_gdn_workspace_bytes", "tree_gdn_fwd")
+            "tree_attn_fwd", "tree_attn_bwd", "tree_gdn_plan", "tree_gdn_workspace_bytes", "tree_gdn_fwd",
+            "tree_mfma_peak")
 
 
 def _check(status: int):
@@ -213,6 +217,13 @@ def _dev(t, name):
 def _stream():
     torch = _torch()
     return torch.cuda.current_stream().cuda_stream
+
+
+def tree_mfma_peak(blocks: int, iters: int, sink) -> float:
+    """Enqueue the matrix-core rate probe on the current stream; returns the flops it performs."""
+    flops = C.c_double(0.0)
+    _check(lib.tree_mfma_peak(int(blocks), int(iters), sink.data_ptr(), C.byref(flops), _stream()))
+    return flops.value
 
 
 def tree_rope(x, pos_ids, theta: float = 10000.0):

@@ -27,6 +27,7 @@ SOURCES = [
     "attn_mfma_bwd.hip",
     "gdn_api.cpp",
     "gdn.hip",
+    "mfma_peak.hip",
 ]
 
 # Packed-fp32 VALU ops are turned off for device code (the compiler would
