@@ -57,8 +57,6 @@ hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, in
                               int32_t* qctr, hipStream_t st);
 // Compute units of the current device (cached per device).
 int mfma_num_cus();
-// Gradient rows of the isolated slots (dq = dk = 0, dv = sum of the group's dout rows).
-hipError_t launch_isolated_bwd(const AttnArgs& a, const int32_t* tiso, hipStream_t st);
 size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D);
 FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D);
 hipError_t mfma_attn_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st);

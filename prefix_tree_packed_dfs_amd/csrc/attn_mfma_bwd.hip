@@ -19,9 +19,10 @@
 //                  S = Q K^T, dP = dout V^T     (A = Q, dout rows from LDS)
 //                  dV^T += dout^T P, dK^T += Q^T dS   (A by transposed LDS
 //                  loads, B = P, dS straight from the S / dP accumulators)
-//   bwd_reduce   sums the partials of split tiles in chunk order;
-//   bwd_isolated the one-key gradients of isolated slots (dq = dk = 0,
-//                dv = the group's dout rows summed).
+//   bwd_reduce   sums the partials of split tiles in chunk order.
+// Work items of bwd_dq whose slots are all isolated (they see and are seen
+// only by themselves) get the one-key gradients from dq_iso_item instead:
+// dq = dk = 0 and dv = the group's dout rows summed.
 // dK/dV and dQ recompute S and dP separately (7 products instead of 5) so
 // that no partial dQ has to be summed across workgroups.
 #include <algorithm>
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
     const int BT = B * TT;
     constexpr int SUB = kKvTile / KT, BPT = kKvTile / 32;  // 64-key tiles, 32-key blocks per KV tile
     const int NQ = Hkv < 8 ? Hkv : 8;
-    // a tile of isolated keys gets no units (bwd_isolated writes its gradients)
+    // a tile of isolated keys gets no units (bwd_dq writes their gradients)
     for (int u = tid; u < BT; u += 1024) {
         const int b = u / TT, t = u % TT;
         int qmax = -1, iso = 1;
@@ -668,7 +669,7 @@ __device__ __forceinline__ void dq_item(const __bf16* __restrict__ q, const __bf
     // the prefetches of later tiles)
     wait_vmcnt<0>();
     {
-        // a block of isolated slots only: dq = 0 is written by bwd_isolated
+        // a block of isolated slots only: its gradients are written by dq_iso_item
         int iso = 1;
         for (int t = i0 / KT; t <= t_last; ++t) iso &= tiso[(int64_t)b * T + t];
         if (iso) return;
@@ -821,6 +822,58 @@ __device__ __forceinline__ void dq_item(const __bf16* __restrict__ q, const __bf
 
 // Persistent dQ: one 512-thread workgroup per CU takes work items from NQ
 // queues, numbered and assigned as in the persistent forward.
+// A dQ work item made of isolated slots only: P = 1 on the diagonal and
+// nothing else, so dS = dout.v - dout.out = 0 and dq = dk = 0; dv of a key is
+// the sum of the dout rows of the G query heads that share its KV head.  The
+// item writes dq = 0 for its BM positions x HB heads and, once per KV head
+// (the item of head chunk 0), dk and dv of its BM positions.  dK/dV and the
+// reduction of split tiles run later and rewrite the keys of tiles they own,
+// with the same values up to rounding.  Out of line, so that the main item's
+// registers are allocated without it.
+template <int D, int HB>
+__device__ __attribute__((noinline)) void dq_iso_item(const __bf16* __restrict__ dout,
+                                                      const int32_t* __restrict__ tiso, int B, int N, int Hq,
+                                                      int Hkv, int T, int n_qtiles, int n_chunks,
+                                                      __bf16* __restrict__ dq, __bf16* __restrict__ dk,
+                                                      __bf16* __restrict__ dv, int item) {
+    constexpr int BM = 256 / HB, LPR = D / 8, RPW = 64 / LPR;
+    const int GH = B * Hkv * n_chunks;
+    const int gi = item % GH, qt = n_qtiles - 1 - item / GH;
+    const int chunk = gi % n_chunks, g = (gi / n_chunks) % Hkv, b = gi / (n_chunks * Hkv);
+    const int G = Hq / Hkv;
+    const int i0 = qt * BM, t_last = (min(i0 + BM, N) - 1) / KT;
+    int iso = 1;
+    for (int t = i0 / KT; t <= t_last; ++t) iso &= tiso[(int64_t)b * T + t];
+    if (!iso) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = (lane % LPR) * 8;
+    const bf16x8 z = {};
+#pragma unroll 4
+    for (int r0 = wave * RPW; r0 < 256; r0 += 8 * RPW) {
+        const int r = r0 + lane / LPR;
+        const int pos = i0 + r / HB, head = g * G + chunk * HB + r % HB;
+        if (pos < N) *reinterpret_cast<bf16x8*>(dq + (((int64_t)b * N + pos) * Hq + head) * D + e) = z;
+    }
+    if (chunk != 0) return;
+    for (int r0 = wave * RPW; r0 < BM; r0 += 8 * RPW) {
+        const int pos = i0 + r0 + lane / LPR;
+        if (pos >= N) continue;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const __bf16* src = dout + (((int64_t)b * N + pos) * Hq + (int64_t)g * G) * D + e;
+        for (int h = 0; h < G; ++h) {
+            const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(src + (int64_t)h * D);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += (float)d8[i];
+        }
+        bf16x8 o;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (__bf16)acc[i];
+        const int64_t kv = (((int64_t)b * N + pos) * Hkv + g) * D + e;
+        *reinterpret_cast<bf16x8*>(dk + kv) = z;
+        *reinterpret_cast<bf16x8*>(dv + kv) = o;
+    }
+}
+
 template <int D, int HB>
 __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                  const __bf16* __restrict__ v, const __bf16* __restrict__ out,
@@ -831,6 +884,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
                                                  const int32_t* __restrict__ tiso,
                                                  int B, int N, int Hq, int Hkv, int T, int n_qtiles, int n_chunks,
                                                  float scale_log2, float scale, __bf16* __restrict__ dq,
+                                                 __bf16* __restrict__ dk, __bf16* __restrict__ dv,
                                                  int* __restrict__ qctr, int NQ, int n_items) {
     constexpr int STAGE = 2 * KT * D * 2 + KT * 4;
     __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];
@@ -844,6 +898,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
         const int item = __builtin_amdgcn_readfirstlane(s_item);
         __syncthreads();
         if (item >= n_items) break;
+        dq_iso_item<D, HB>(dout, tiso, B, N, Hq, Hkv, T, n_qtiles, n_chunks, dq, dk, dv, item);
         dq_item<D, HB>(q, k, v, out, dout, lse, delta, lse2, se, tmin, tmax, tiso, B, N, Hq, Hkv, T, n_qtiles,
                        n_chunks, scale_log2, scale, dq, item, smem, list, list_meta);
         __syncthreads();  // the stages and the list are reused by the next item
@@ -862,7 +917,8 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
     hipLaunchKernelGGL((bwd_dq<D, HB>), dim3((unsigned)grid), dim3(512), 0, st, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.out, (const __bf16*)a.dout, a.lse,
                        w.delta, w.lse2, a.se, w.tile_min, w.tile_max, w.tile_iso, a.B, a.N, a.Hq, a.Hkv, T,
-                       n_qtiles, n_chunks, a.scale * kLog2e, a.scale, (__bf16*)a.dq, w.qctr, NQ, (int)items);
+                       n_qtiles, n_chunks, a.scale * kLog2e, a.scale, (__bf16*)a.dq, (__bf16*)a.dk, (__bf16*)a.dv,
+                       w.qctr, NQ, (int)items);
     return hipGetLastError();
 }
 
@@ -893,8 +949,7 @@ hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) 
                        w.split_tiles, w.partial, a.N, a.Hkv, (__bf16*)a.dk, (__bf16*)a.dv);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // last: exact rows of the isolated slots (over whatever the kernels above wrote for them)
-    return launch_isolated_bwd(a, w.tile_iso, st);
+    return hipSuccess;
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }

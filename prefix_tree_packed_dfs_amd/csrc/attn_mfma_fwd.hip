@@ -17,8 +17,8 @@
 //     keeps its Q fragments in registers;
 //   * the kernel is persistent: one workgroup per CU takes items from
 //     per-XCD queues, deepest query block first.
-// Slots that see and are seen only by themselves (padding, one-token
-// sequences) are left to fwd_isolated, which writes their one-key result.
+// An item whose slots all see and are seen only by themselves (padding,
+// one-token sequences) gets the one-key result from fwd_iso_item instead.
 // Products are v_mfma_f32_32x32x16_bf16 in the transposed orientation:
 //   S^T = K Q^T   (A = K from LDS, B = Q^T from registers)
 //   O^T += V^T P^T (A = V^T from LDS, B = P^T straight from the S^T accumulator)
@@ -108,95 +108,6 @@ __global__ __launch_bounds__(1024) void iso_scan(const int32_t* __restrict__ tma
     }
 }
 
-// Isolated slots of the forward: a query that sees only itself has a one-term
-// softmax, so out = v and lse = scale q.k.  Grid (T, kIsoSplit, B), 256
-// threads; tiles that are not isolated return at once.  The (slot, head) rows
-// of a tile are split over kIsoSplit workgroups, D / 8 lanes per row.
-constexpr int kIsoSplit = 8;
-
-template <int D>
-__global__ __launch_bounds__(256) void fwd_isolated(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                                                    const __bf16* __restrict__ v, const int32_t* __restrict__ tiso,
-                                                    int B, int N, int Hq, int Hkv, int T, float scale,
-                                                    __bf16* __restrict__ out, float* __restrict__ lse) {
-    constexpr int LPR = D / 8, RPW = 64 / LPR;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int G = Hq / Hkv, rows = KT * Hq / kIsoSplit;
-    const int e = (lane % LPR) * 8;
-    // work (row, tile, part of the tile); the grid strides over it
-    for (int64_t wk = blockIdx.x; wk < (int64_t)B * T * kIsoSplit; wk += gridDim.x) {
-    const int t = (int)(wk / kIsoSplit % T), b = (int)(wk / kIsoSplit / T);
-    if (!tiso[(int64_t)b * T + t]) continue;
-    const int rbase = (int)(wk % kIsoSplit) * rows;
-#pragma unroll 4
-    for (int r0 = rbase + wave * RPW; r0 < rbase + rows; r0 += 4 * RPW) {
-        const int r = r0 + lane / LPR;
-        const int slot = t * KT + r / Hq, h = r % Hq;
-        const int sc = min(slot, N - 1);
-        const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(q + (((int64_t)b * N + sc) * Hq + h) * D + e);
-        const int64_t kv = (((int64_t)b * N + sc) * Hkv + h / G) * D + e;
-        const bf16x8 k8 = *reinterpret_cast<const bf16x8*>(k + kv);
-        const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(v + kv);
-        float dot = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dot = fmaf((float)q8[i], (float)k8[i], dot);
-#pragma unroll
-        for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o, 64);
-        if (slot < N) {
-            *reinterpret_cast<bf16x8*>(out + (((int64_t)b * N + slot) * Hq + h) * D + e) = v8;
-            if (lane % LPR == 0) lse[((int64_t)b * Hq + h) * N + slot] = dot * scale;
-        }
-    }
-    }
-}
-
-// Isolated slots of the backward: P = 1 on the diagonal and nothing else, so
-// dS = P (dP - delta) = dout.v - dout.out = 0: dq = dk = 0, and dv is the sum of
-// the dout rows of the query heads sharing the key's head.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_isolated(const __bf16* __restrict__ dout,
-                                                    const int32_t* __restrict__ tiso, int B, int N, int Hq, int Hkv,
-                                                    int T, __bf16* __restrict__ dq, __bf16* __restrict__ dk,
-                                                    __bf16* __restrict__ dv) {
-    constexpr int LPR = D / 8, RPW = 64 / LPR;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int G = Hq / Hkv;
-    const int e = (lane % LPR) * 8;
-    const bf16x8 z = {};
-    for (int64_t wk = blockIdx.x; wk < (int64_t)B * T * kIsoSplit; wk += gridDim.x) {
-    const int t = (int)(wk / kIsoSplit % T), b = (int)(wk / kIsoSplit / T);
-    if (!tiso[(int64_t)b * T + t]) continue;
-    const int part = (int)(wk % kIsoSplit);
-    const int qrows = KT * Hq / kIsoSplit, qbase = part * qrows;
-#pragma unroll 4
-    for (int r0 = qbase + wave * RPW; r0 < qbase + qrows; r0 += 4 * RPW) {  // dq rows
-        const int r = r0 + lane / LPR;
-        const int slot = t * KT + r / Hq;
-        if (slot < N) *reinterpret_cast<bf16x8*>(dq + (((int64_t)b * N + slot) * Hq + r % Hq) * D + e) = z;
-    }
-    const int kvrows = KT * Hkv / kIsoSplit, kvbase = part * kvrows;
-#pragma unroll 4
-    for (int r0 = kvbase + wave * RPW; r0 < kvbase + kvrows; r0 += 4 * RPW) {  // dk, dv rows
-        const int r = r0 + lane / LPR;
-        const int slot = t * KT + r / Hkv, g = r % Hkv;
-        if (slot >= N) continue;
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        const __bf16* src = dout + (((int64_t)b * N + slot) * Hq + (int64_t)g * G) * D + e;
-        for (int h = 0; h < G; ++h) {
-            const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(src + (int64_t)h * D);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += (float)d8[i];
-        }
-        bf16x8 o;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = (__bf16)acc[i];
-        const int64_t kv = (((int64_t)b * N + slot) * Hkv + g) * D + e;
-        *reinterpret_cast<bf16x8*>(dk + kv) = z;
-        *reinterpret_cast<bf16x8*>(dv + kv) = o;
-    }
-    }
-}
-
 // One work item of the forward: BM positions x HB query heads of one KV head.
 template <int D, int HB>
 __device__ __forceinline__ void fwd_item(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -234,7 +145,7 @@ __device__ __forceinline__ void fwd_item(const __bf16* __restrict__ q, const __b
     const int i_last = min(i0 + BM, N) - 1;
     const int t_last = i_last / KT;
     {
-        // a block of isolated slots only is written by fwd_isolated
+        // a block of isolated slots only is written by fwd_iso_item
         int iso = 1;
         for (int t = i0 / KT; t <= t_last; ++t) iso &= tiso[(int64_t)b * T + t];
         if (iso) return;
@@ -457,6 +368,48 @@ __device__ __forceinline__ void fwd_item(const __bf16* __restrict__ q, const __b
     }
 }
 
+// A forward work item made of isolated slots only: the one-term softmax,
+// out = v and lse = scale q.k, for its BM positions x HB query heads; 16 lanes
+// (D / 8) per (position, head) row.  Out of line, so that the main item's
+// registers are allocated without it.  Returns at once for other items.
+template <int D, int HB>
+__device__ __attribute__((noinline)) void fwd_iso_item(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                       const __bf16* __restrict__ v, const int32_t* __restrict__ tiso,
+                                                       int B, int N, int Hq, int Hkv, int T, int n_qtiles,
+                                                       int n_chunks, float scale, __bf16* __restrict__ out,
+                                                       float* __restrict__ lse, int item) {
+    constexpr int BM = 256 / HB, LPR = D / 8, RPW = 64 / LPR;
+    const int GH = B * Hkv * n_chunks;
+    const int gi = item % GH, qt = n_qtiles - 1 - item / GH;
+    const int chunk = gi % n_chunks, g = (gi / n_chunks) % Hkv, b = gi / (n_chunks * Hkv);
+    const int G = Hq / Hkv;
+    const int i0 = qt * BM, t_last = (min(i0 + BM, N) - 1) / KT;
+    int iso = 1;
+    for (int t = i0 / KT; t <= t_last; ++t) iso &= tiso[(int64_t)b * T + t];
+    if (!iso) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = (lane % LPR) * 8;
+#pragma unroll 4
+    for (int r0 = wave * RPW; r0 < 256; r0 += 8 * RPW) {
+        const int r = r0 + lane / LPR;
+        const int pos = i0 + r / HB, head = g * G + chunk * HB + r % HB;
+        const int pc = min(pos, N - 1);
+        const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(q + (((int64_t)b * N + pc) * Hq + head) * D + e);
+        const int64_t kv = (((int64_t)b * N + pc) * Hkv + g) * D + e;
+        const bf16x8 k8 = *reinterpret_cast<const bf16x8*>(k + kv);
+        const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(v + kv);
+        float dot = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dot = fmaf((float)q8[i], (float)k8[i], dot);
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o, 64);
+        if (pos < N) {
+            *reinterpret_cast<bf16x8*>(out + (((int64_t)b * N + pos) * Hq + head) * D + e) = v8;
+            if (lane % LPR == 0) lse[((int64_t)b * Hq + head) * N + pos] = dot * scale;
+        }
+    }
+}
+
 // Persistent forward: one 512-thread workgroup per CU takes work items from
 // NQ queues (workgroup w serves queue w mod NQ; queue x holds items x, x + NQ,
 // ...).  Items are numbered deepest query block first, with the KV head
@@ -469,7 +422,7 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
                                                    const int32_t* __restrict__ tmax,
                                                    const int32_t* __restrict__ tiso, int B, int N, int Hq,
                                                    int Hkv, int T, int n_qtiles, int n_chunks, float scale_log2,
-                                                   __bf16* __restrict__ out, float* __restrict__ lse,
+                                                   float scale, __bf16* __restrict__ out, float* __restrict__ lse,
                                                    int* __restrict__ qctr, int NQ, int n_items) {
     constexpr int STAGE = 2 * KT * D * 2 + KT * 4;
     __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];
@@ -483,16 +436,11 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
         const int item = __builtin_amdgcn_readfirstlane(s_item);
         __syncthreads();
         if (item >= n_items) break;
+        fwd_iso_item<D, HB>(q, k, v, tiso, B, N, Hq, Hkv, T, n_qtiles, n_chunks, scale, out, lse, item);
         fwd_item<D, HB>(q, k, v, se, tmin, tmax, tiso, B, N, Hq, Hkv, T, n_qtiles, n_chunks, scale_log2, out, lse,
                         item, smem, list, list_meta);
         __syncthreads();  // the stages and the list are reused by the next item
     }
-}
-
-// Workgroups of the isolated-slot kernels: enough to keep every CU streaming,
-// never more than there is work (B * T tiles x kIsoSplit parts).
-unsigned iso_grid(int B, int T) {
-    return (unsigned)std::min<int64_t>((int64_t)B * T * kIsoSplit, 8 * (int64_t)mfma_num_cus());
 }
 
 template <int D, int HB>
@@ -507,8 +455,8 @@ hipError_t launch_main(const AttnArgs& a, const FwdWorkspace& w, int T, hipStrea
     const float scale_log2 = a.scale * 1.4426950408889634f;
     hipLaunchKernelGGL((fwd_main<D, HB>), dim3((unsigned)grid), dim3(512), 0, st, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, a.se, w.tile_min, w.tile_max, w.tile_iso, a.B,
-                       a.N, a.Hq, a.Hkv, T, n_qtiles, n_chunks, scale_log2, (__bf16*)a.out, a.lse, w.qctr, NQ,
-                       (int)items);
+                       a.N, a.Hq, a.Hkv, T, n_qtiles, n_chunks, scale_log2, a.scale, (__bf16*)a.out, a.lse,
+                       w.qctr, NQ, (int)items);
     return hipGetLastError();
 }
 
@@ -524,10 +472,7 @@ hipError_t launch_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st) 
         default: e = launch_main<D, 8>(a, w, T, st); break;
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fwd_isolated<D>), dim3(iso_grid(a.B, T)), dim3(256), 0, st, (const __bf16*)a.q,
-                       (const __bf16*)a.k, (const __bf16*)a.v, w.tile_iso, a.B, a.N, a.Hq, a.Hkv, T, a.scale,
-                       (__bf16*)a.out, a.lse);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -564,17 +509,6 @@ hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, in
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(iso_scan, dim3(B), dim3(1024), 0, st, tmax, T, tiso);
-    return hipGetLastError();
-}
-
-hipError_t launch_isolated_bwd(const AttnArgs& a, const int32_t* tiso, hipStream_t st) {
-    const int T = (a.N + KT - 1) / KT;
-    if (a.D == 64)
-        hipLaunchKernelGGL((bwd_isolated<64>), dim3(iso_grid(a.B, T)), dim3(256), 0, st, (const __bf16*)a.dout,
-                           tiso, a.B, a.N, a.Hq, a.Hkv, T, (__bf16*)a.dq, (__bf16*)a.dk, (__bf16*)a.dv);
-    else
-        hipLaunchKernelGGL((bwd_isolated<128>), dim3(iso_grid(a.B, T)), dim3(256), 0, st, (const __bf16*)a.dout,
-                           tiso, a.B, a.N, a.Hq, a.Hkv, T, (__bf16*)a.dq, (__bf16*)a.dk, (__bf16*)a.dv);
     return hipGetLastError();
 }
 

@@ -94,8 +94,10 @@ __device__ __forceinline__ int next_visible(const int32_t* __restrict__ tmaxb, i
 // order, so the compiler's own waits for older loads stay correct.
 // LDS byte address of a pointer into shared memory, as a wave-uniform scalar
 // (callers pass per-wave bases; readfirstlane puts them in an SGPR for M0).
+// The low 32 bits of a generic address inside the LDS aperture are the LDS
+// offset, so no address-space cast (and the null test it implies) is needed.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds_addr(lds_base))
