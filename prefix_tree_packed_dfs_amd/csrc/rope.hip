@@ -8,9 +8,10 @@
 // HBM-bound: every element is read once and written once.  A thread owns four
 // (fp32) or eight (bf16: 16-byte accesses) consecutive frequencies of one slot
 // and walks over the heads, so its sines and cosines are computed once and
-// reused H times.  They are computed in fp64
-// (the angle reaches tens of thousands of radians at depth 36K, where an fp32
-// angle would already be off by ~1e-3) and rounded once to the storage type.
+// reused H times.  The angle reaches tens of thousands of radians at depth
+// 36K, where an fp32 angle would already be off by ~1e-3, so it is formed in
+// fp64: for fp32 storage the whole rotation is fp64, for bf16 the fp64 angle
+// is reduced to [-pi, pi] and its sine and cosine are taken in fp32.
 // A slot at depth 0 (a root, or a padding slot) turns by angle 0, which is the
 // identity, so its rows are neither read nor written.
 #include "common.h"
@@ -31,53 +32,70 @@ __global__ __launch_bounds__(256) void rope_kernel_bf16(__bf16* __restrict__ x, 
     if (slot >= BN) return;
     const int p_i = pos[slot];
     if (p_i == 0) return;  // identity
+    __bf16* row = x + slot * (int64_t)H * D + oct * 8;
+    // the first group of heads is loaded before the angles are computed
+    constexpr int HG = 4;
+    bf16x8 va[HG], vb[HG];
+    const int h0 = min(H, HG);
+#pragma unroll
+    for (int e = 0; e < HG; ++e)
+        if (e < h0) {
+            va[e] = *reinterpret_cast<const bf16x8*>(row + (int64_t)e * D);
+            vb[e] = *reinterpret_cast<const bf16x8*>(row + (int64_t)e * D + HALF);
+        }
+    // Angle p * theta^(-2i/D) in fp64, reduced to [-pi, pi] in fp64 (the
+    // product and the reduction are exact to ~1e-11 rad at any depth), then
+    // sine and cosine of the reduced angle in fp32 (errors near 1e-7, far
+    // below half a bf16 ulp).  Frequencies: one exp2 per thread, then the
+    // constant ratio theta^(-2/D) between neighbours.
     const double p = (double)p_i;
+    const double ratio = exp2(-2.0 / (double)D * log2_theta);
+    double f = exp2(-(double)(16 * oct) / (double)D * log2_theta);
+    constexpr double kTwoPi = 6.283185307179586;
+    constexpr double kInvTwoPi = 0.15915494309189535;
     float c[8], s[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-        const int i = oct * 8 + u;
-        // theta^(-2i/D) = 2^(-(2i/D) log2 theta)
-        const double ang = p * exp2(-(double)(2 * i) / (double)D * log2_theta);
-        double sd, cd;
-        sincos(ang, &sd, &cd);
-        c[u] = (float)cd;
-        s[u] = (float)sd;
+        const double ang = p * f;
+        const double r = fma(-rint(ang * kInvTwoPi), kTwoPi, ang);
+        // sine and cosine of the fp32 head of the angle, corrected to first
+        // order by its fp32 tail (the tail is below 2e-7 rad)
+        const float rh = (float)r, rl = (float)(r - (double)rh);
+        float sh, ch;
+        sincosf(rh, &sh, &ch);
+        s[u] = fmaf(ch, rl, sh);
+        c[u] = fmaf(-sh, rl, ch);
+        f *= ratio;
     }
     // fp32 products are enough for bf16 storage: one rounding of an fp32
     // expression whose error is far below half a bf16 ulp.
-    __bf16* row = x + slot * (int64_t)H * D + oct * 8;
-    auto rotate = [&](const bf16x8& va, const bf16x8& vb, bf16x8& ra, bf16x8& rb) {
+    auto rotate = [&](const bf16x8& a, const bf16x8& b, bf16x8& ra, bf16x8& rb) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const float xa = (float)va[u], xb = (float)vb[u];
+            const float xa = (float)a[u], xb = (float)b[u];
             ra[u] = (__bf16)(xa * c[u] - xb * s[u]);
             rb[u] = (__bf16)(xb * c[u] + xa * s[u]);
         }
     };
-    // heads in groups of four: all loads of a group are in flight together
-    int h = 0;
-    for (; h + 4 <= H; h += 4) {
-        bf16x8 va[4], vb[4];
+    for (int h = 0;;) {
+        const int n = min(HG, H - h);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            va[e] = *reinterpret_cast<const bf16x8*>(row + (int64_t)(h + e) * D);
-            vb[e] = *reinterpret_cast<const bf16x8*>(row + (int64_t)(h + e) * D + HALF);
-        }
+        for (int e = 0; e < HG; ++e)
+            if (e < n) {
+                bf16x8 ra, rb;
+                rotate(va[e], vb[e], ra, rb);
+                *reinterpret_cast<bf16x8*>(row + (int64_t)(h + e) * D) = ra;
+                *reinterpret_cast<bf16x8*>(row + (int64_t)(h + e) * D + HALF) = rb;
+            }
+        h += HG;
+        if (h >= H) break;
+        const int m = min(HG, H - h);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            bf16x8 ra, rb;
-            rotate(va[e], vb[e], ra, rb);
-            *reinterpret_cast<bf16x8*>(row + (int64_t)(h + e) * D) = ra;
-            *reinterpret_cast<bf16x8*>(row + (int64_t)(h + e) * D + HALF) = rb;
-        }
-    }
-    for (; h < H; ++h) {
-        bf16x8* a = reinterpret_cast<bf16x8*>(row + (int64_t)h * D);
-        bf16x8* b = reinterpret_cast<bf16x8*>(row + (int64_t)h * D + HALF);
-        bf16x8 ra, rb;
-        rotate(*a, *b, ra, rb);
-        *a = ra;
-        *b = rb;
+        for (int e = 0; e < HG; ++e)
+            if (e < m) {
+                va[e] = *reinterpret_cast<const bf16x8*>(row + (int64_t)(h + e) * D);
+                vb[e] = *reinterpret_cast<const bf16x8*>(row + (int64_t)(h + e) * D + HALF);
+            }
     }
 }
 
