@@ -8,11 +8,12 @@
 // Kernels, in launch order, no atomics on results (bitwise reproducible):
 //   tile ranges  min / max subtree_end per 64-key tile and which tiles hold
 //                isolated slots only (shared with the forward);
-//   bwd_plan     the dK/dV work plan (split long KV tiles, per-XCD queues);
 //   bwd_dq       query-stationary and persistent, shaped like the forward:
 //                S^T = K Q^T and dP^T = V dout^T with Q, dout in registers,
 //                then dQ^T += K^T dS^T with dS^T taken from the accumulator;
-//                it also writes delta and lse * log2(e) for the next kernel;
+//                it also writes delta and lse * log2(e) for the next kernel,
+//                and one of its workgroups first writes the dK/dV work plan
+//                (split long KV tiles, per-XCD queues);
 //   bwd_dkdv     KV-stationary and persistent: a workgroup owns 256 keys of
 //                one KV head (32 per wave) and walks the query blocks its
 //                keys can see, for every query head of the group:
@@ -45,7 +46,7 @@ __device__ __forceinline__ T ld16(const void* p) {
 
 
 // ---------------------------------------------------------------------------
-// dK/dV work plan (one workgroup).  A KV tile of kKvTile keys visits every
+// dK/dV work plan (one workgroup of the dQ kernel).  A KV tile of kKvTile keys visits every
 // (32-position block, query head) pair from its first key's block to the
 // block of the largest subtree_end among its keys.  Keys of a long shared
 // prefix visit almost the whole row while keys near the leaves visit a few
@@ -60,9 +61,12 @@ __device__ __forceinline__ T ld16(const void* p) {
 // ---------------------------------------------------------------------------
 constexpr int kPlanBuckets = 4096;
 
-// Exclusive prefix sum over the 1024 threads of the workgroup: inside each
-// wave by shuffles, then over the 16 wave totals (s_scan holds at least 16 ints).
+// Exclusive prefix sum over the NT threads of the workgroup: inside each wave
+// by shuffles, then over the NT / 64 wave totals (s_scan holds at least that
+// many ints).
+template <int NT>
 __device__ int block_exclusive_scan(int v, int* s_scan) {
+    constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int x = v;
 #pragma unroll
@@ -73,13 +77,13 @@ __device__ int block_exclusive_scan(int v, int* s_scan) {
     if (lane == 63) s_scan[wave] = x;
     __syncthreads();
     if (wave == 0) {
-        int t = lane < 16 ? s_scan[lane] : 0;
+        int t = lane < NW ? s_scan[lane] : 0;
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
+        for (int off = 1; off < NW; off <<= 1) {
             const int y = __shfl_up(t, off, 64);
             if (lane >= off) t += y;
         }
-        if (lane < 16) s_scan[lane] = t;  // inclusive totals of waves 0..lane
+        if (lane < NW) s_scan[lane] = t;  // inclusive totals of waves 0..lane
     }
     __syncthreads();
     const int r = x - v + (wave > 0 ? s_scan[wave - 1] : 0);
@@ -87,20 +91,26 @@ __device__ int block_exclusive_scan(int v, int* s_scan) {
     return r;
 }
 
-__global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tmax, const int32_t* __restrict__ tiso,
-                                                 int B, int N, int T, int G, int Hkv, int* __restrict__ ctrl,
-                                                 int4* __restrict__ tile_plan, int4* __restrict__ units,
-                                                 int4* __restrict__ split_tiles) {
-    __shared__ int s_sum, s_budget;
-    __shared__ int s_scan[1024];
-    __shared__ int s_cnt[kPlanBuckets];
+// The plan, computed by the NT threads of one workgroup.  lds: at least
+// kPlanLds ints of shared memory the workgroup does not otherwise use meanwhile.
+constexpr int kPlanLds = 64 + kPlanBuckets;
+
+template <int NT>
+__device__ void make_plan(const int32_t* __restrict__ tmax, const int32_t* __restrict__ tiso, int B, int N, int T,
+                          int G, int Hkv, int* __restrict__ ctrl, int4* __restrict__ tile_plan,
+                          int4* __restrict__ units, int4* __restrict__ split_tiles, int* lds) {
+    static_assert(kPlanBuckets % NT == 0 && NT % 64 == 0 && NT / 64 <= 48, "bucket scan layout");
+    int& s_sum = lds[0];
+    int& s_budget = lds[1];
+    int* s_scan = lds + 16;
+    int* s_cnt = lds + 64;
     const int tid = threadIdx.x;
     const int TT = (N + kKvTile - 1) / kKvTile;  // KV tiles per row
     const int BT = B * TT;
     constexpr int SUB = kKvTile / KT, BPT = kKvTile / 32;  // 64-key tiles, 32-key blocks per KV tile
     const int NQ = Hkv < 8 ? Hkv : 8;
     // a tile of isolated keys gets no units (bwd_dq writes their gradients)
-    for (int u = tid; u < BT; u += 1024) {
+    for (int u = tid; u < BT; u += NT) {
         const int b = u / TT, t = u % TT;
         int qmax = -1, iso = 1;
         for (int x = SUB * t; x < min(SUB * t + SUB, T); ++x) {
@@ -117,7 +127,7 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
         __syncthreads();
         C = max(1, s_budget / G);
         int part = 0;
-        for (int u = tid; u < BT; u += 1024) {
+        for (int u = tid; u < BT; u += NT) {
             const int4 e = tile_plan[u];
             if (e.y - e.x + 1 > C) part += e.y / C - e.x / C + 1;
         }
@@ -130,7 +140,7 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
         __syncthreads();
     }
     // chunks per tile; slots and split-tile indices by an exclusive scan in tile order
-    const int per = (BT + 1023) / 1024;
+    const int per = (BT + NT - 1) / NT;
     const int u0 = min(BT, tid * per), u1 = min(BT, u0 + per);
     int my_chunks = 0, my_split = 0, my_units = 0;
     for (int u = u0; u < u1; ++u) {
@@ -143,10 +153,10 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
         my_units += nc;
     }
     // chunk and split counts are at most kSplitSlots: pack both in one scan
-    const int packed = block_exclusive_scan(my_chunks | (my_split << 16), s_scan);
+    const int packed = block_exclusive_scan<NT>(my_chunks | (my_split << 16), s_scan);
     const int n_units = [&] {
-        const int before = block_exclusive_scan(my_units, s_scan);
-        if (tid == 1023) s_sum = before + my_units;
+        const int before = block_exclusive_scan<NT>(my_units, s_scan);
+        if (tid == NT - 1) s_sum = before + my_units;
         __syncthreads();
         return s_sum;
     }();
@@ -164,7 +174,7 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
             }
             tile_plan[u] = e;
         }
-        if (tid == 1023) {
+        if (tid == NT - 1) {
             ctrl[24] = z;
             int start = 0;
             for (int x = 0; x < NQ; ++x) {
@@ -190,25 +200,26 @@ __global__ __launch_bounds__(1024) void bwd_plan(const int32_t* __restrict__ tma
     };
     int shift = 0;
     while (((NKEY - 1) >> shift) >= kPlanBuckets) ++shift;
-    for (int x = tid; x < kPlanBuckets; x += 1024) s_cnt[x] = 0;
+    for (int x = tid; x < kPlanBuckets; x += NT) s_cnt[x] = 0;
     __syncthreads();
     for (int u = u0; u < u1; ++u) {
         const int4 e = tile_plan[u];
         for (int kk = 0; kk < e.z; ++kk) atomicAdd(&s_cnt[ukey(e, kk) >> shift], 1);
     }
     __syncthreads();
-    {  // exclusive scan of the bucket counts, four per thread
-        int c4[4], s = 0;
+    {  // exclusive scan of the bucket counts, PB per thread
+        constexpr int PB = kPlanBuckets / NT;
+        int cb[PB], s = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            c4[i] = s_cnt[4 * tid + i];
-            s += c4[i];
+        for (int i = 0; i < PB; ++i) {
+            cb[i] = s_cnt[PB * tid + i];
+            s += cb[i];
         }
-        int off = block_exclusive_scan(s, s_scan);
+        int off = block_exclusive_scan<NT>(s, s_scan);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s_cnt[4 * tid + i] = off;
-            off += c4[i];
+        for (int i = 0; i < PB; ++i) {
+            s_cnt[PB * tid + i] = off;
+            off += cb[i];
         }
     }
     __syncthreads();
@@ -822,6 +833,25 @@ __device__ __forceinline__ void dq_item(const __bf16* __restrict__ q, const __bf
 
 // Persistent dQ: one 512-thread workgroup per CU takes work items from NQ
 // queues, numbered and assigned as in the persistent forward.
+// Arguments of the dK/dV plan, passed through the dQ kernel that computes it.
+struct PlanArgs {
+    const int32_t* tmax;
+    const int32_t* tiso;
+    int B, N, T, G, Hkv;
+    int* ctrl;
+    int4* tile_plan;
+    int4* units;
+    int4* split_tiles;
+};
+
+// The plan by one 512-thread workgroup of the dQ kernel; out of line, so the
+// dQ items' registers are allocated without it.
+__device__ __attribute__((noinline)) void plan_in_wg(const int32_t* tmax, const int32_t* tiso, int B, int N, int T,
+                                                     int G, int Hkv, int* ctrl, int4* tile_plan, int4* units,
+                                                     int4* split_tiles, int* lds) {
+    make_plan<512>(tmax, tiso, B, N, T, G, Hkv, ctrl, tile_plan, units, split_tiles, lds);
+}
+
 // A dQ work item made of isolated slots only: P = 1 on the diagonal and
 // nothing else, so dS = dout.v - dout.out = 0 and dq = dk = 0; dv of a key is
 // the sum of the dout rows of the G query heads that share its KV head.  The
@@ -885,13 +915,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
                                                  int B, int N, int Hq, int Hkv, int T, int n_qtiles, int n_chunks,
                                                  float scale_log2, float scale, __bf16* __restrict__ dq,
                                                  __bf16* __restrict__ dk, __bf16* __restrict__ dv,
-                                                 int* __restrict__ qctr, int NQ, int n_items) {
+                                                 int* __restrict__ qctr, int NQ, int n_items, PlanArgs plan) {
     constexpr int STAGE = 2 * KT * D * 2 + KT * 4;
     __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];
     __shared__ int list[1024];
     __shared__ int list_meta[2];
     __shared__ int s_item;
     const int qx = blockIdx.x % NQ;
+    // the last workgroup first writes the dK/dV plan (read only by the next
+    // kernel); the others meanwhile take its share of the items
+    if (blockIdx.x == gridDim.x - 1) {
+        static_assert(kPlanLds * 4 <= 4 * STAGE, "plan scratch fits the stages");
+        plan_in_wg(plan.tmax, plan.tiso, plan.B, plan.N, plan.T, plan.G, plan.Hkv, plan.ctrl, plan.tile_plan,
+                   plan.units, plan.split_tiles, reinterpret_cast<int*>(smem));
+        __syncthreads();
+    }
     for (;;) {
         if (threadIdx.x == 0) s_item = qx + NQ * atomicAdd(&qctr[qx], 1);
         __syncthreads();
@@ -918,7 +956,9 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.out, (const __bf16*)a.dout, a.lse,
                        w.delta, w.lse2, a.se, w.tile_min, w.tile_max, w.tile_iso, a.B, a.N, a.Hq, a.Hkv, T,
                        n_qtiles, n_chunks, a.scale * kLog2e, a.scale, (__bf16*)a.dq, (__bf16*)a.dk, (__bf16*)a.dv,
-                       w.qctr, NQ, (int)items);
+                       w.qctr, NQ, (int)items,
+                       PlanArgs{w.tile_max, w.tile_iso, a.B, a.N, T, a.Hq / a.Hkv, a.Hkv, w.ctrl, w.tile_plan, w.units,
+                                w.split_tiles});
     return hipGetLastError();
 }
 
@@ -926,10 +966,6 @@ template <int D>
 hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
     hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, w.tile_iso, w.qctr, st);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_plan, dim3(1), dim3(1024), 0, st, w.tile_max, w.tile_iso, a.B, a.N, T, a.Hq / a.Hkv,
-                       a.Hkv, w.ctrl, w.tile_plan, w.units, w.split_tiles);
-    e = hipGetLastError();
     if (e != hipSuccess) return e;
     // dQ first: it also writes delta and lse * log2(e), which dK/dV reads
     switch (heads_per_wg(a.Hq / a.Hkv)) {
