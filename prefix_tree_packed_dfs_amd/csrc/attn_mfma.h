@@ -11,6 +11,12 @@ namespace treeattn {
 constexpr int KT = 64;
 // Work queues of the persistent query-stationary kernels (one per XCD).
 constexpr int kItemQueues = 8;
+// Work-queue counters after the item queues: the isolated-slot unit queue and
+// the number of isolated tiles listed.  An isolated tile is kIsoSplit units.
+constexpr int kIsoQueue = kItemQueues;
+constexpr int kIsoCount = kItemQueues + 1;
+constexpr int kQueueCounters = kItemQueues + 2;
+constexpr int kIsoSplit = 8;
 
 // Query heads one workgroup serves (all heads sharing a KV head, up to 8).
 inline int heads_per_wg(int G) { return G >= 8 ? 8 : G; }
@@ -24,7 +30,8 @@ struct FwdWorkspace {
     int32_t* tile_min;   // [B, T]
     int32_t* tile_max;   // [B, T]
     int32_t* tile_iso;   // [B, T] 1 if every slot of the tile is isolated (sees and is seen by itself only)
-    int32_t* qctr;       // [kItemQueues] work-queue counters of the persistent forward
+    int32_t* iso_list;   // [B * T] the isolated tiles, b * T + t, in no particular order
+    int32_t* qctr;       // [kQueueCounters] work-queue counters of the persistent forward
 };
 
 // Workspace carved by the backward.
@@ -34,7 +41,8 @@ struct BwdWorkspace {
     int32_t* tile_min;   // [B, T]
     int32_t* tile_max;   // [B, T]
     int32_t* tile_iso;   // [B, T]
-    int32_t* qctr;       // [kItemQueues] work-queue counters of the persistent dQ kernel
+    int32_t* iso_list;   // [B * T]
+    int32_t* qctr;       // [kQueueCounters] work-queue counters of the persistent dQ kernel
     // dK/dV work plan: KV tiles of 256 keys whose query range is long are split
     // into chunks of visits; chunks write fp32 partials that a reduce pass sums
     int32_t* ctrl;       // queue counters / lengths / starts, split-tile count
@@ -51,10 +59,11 @@ constexpr int kSplitSlots = 1536 * 256 / kKvTile;
 constexpr int kVisitBudget = 384;
 
 // Smallest and largest subtree_end of every KT-key tile of each row ([B, T]),
-// and whether every slot of the tile is isolated.
-// (Also zeroes the kItemQueues work-queue counters at qctr.)
+// and whether every slot of the tile is isolated; the isolated tiles listed
+// in iso_list, their number in qctr[kIsoCount].
+// (Also zeroes the kQueueCounters work-queue counters at qctr first.)
 hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, int32_t* tmax, int32_t* tiso,
-                              int32_t* qctr, hipStream_t st);
+                              int32_t* iso_list, int32_t* qctr, hipStream_t st);
 // Compute units of the current device (cached per device).
 int mfma_num_cus();
 size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D);

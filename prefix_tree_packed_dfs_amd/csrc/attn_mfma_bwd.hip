@@ -21,9 +21,10 @@
 //                  dV^T += dout^T P, dK^T += Q^T dS   (A by transposed LDS
 //                  loads, B = P, dS straight from the S / dP accumulators)
 //   bwd_reduce   sums the partials of split tiles in chunk order.
-// Work items of bwd_dq whose slots are all isolated (they see and are seen
-// only by themselves) get the one-key gradients from dq_iso_item instead:
-// dq = dk = 0 and dv = the group's dout rows summed.
+// Tiles whose slots are all isolated (they see and are seen only by
+// themselves) get the one-key gradients from isolated-slot units, one of
+// which a dQ workgroup takes after each item of matrix work: dq = dk = 0 and
+// dv = the group's dout rows summed.
 // dK/dV and dQ recompute S and dP separately (7 products instead of 5) so
 // that no partial dQ has to be summed across workgroups.
 #include <algorithm>
@@ -600,7 +601,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
 // ---------------------------------------------------------------------------
 // One work item of dQ: BM positions x HB query heads of one KV head.
 template <int D, int HB>
-__device__ __forceinline__ void dq_item(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+__device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                         const __bf16* __restrict__ v, const __bf16* __restrict__ out,
                                         const __bf16* __restrict__ dout, const float* __restrict__ lse,
                                         float* __restrict__ delta, float* __restrict__ lse2,
@@ -680,10 +681,11 @@ __device__ __forceinline__ void dq_item(const __bf16* __restrict__ q, const __bf
     // the prefetches of later tiles)
     wait_vmcnt<0>();
     {
-        // a block of isolated slots only: its gradients are written by dq_iso_item
+        // a block of isolated slots only: its gradients are written by the
+        // isolated-slot units
         int iso = 1;
         for (int t = i0 / KT; t <= t_last; ++t) iso &= tiso[(int64_t)b * T + t];
-        if (iso) return;
+        if (iso) return false;
     }
     f32x16 acc[NDB];
 #pragma unroll
@@ -817,7 +819,8 @@ __device__ __forceinline__ void dq_item(const __bf16* __restrict__ q, const __bf
         }
         __syncthreads();
     }
-    if (ip < N) {
+    // rows of isolated tiles belong to the isolated-slot units
+    if (ip < N && !tiso[(int64_t)b * T + ip / KT]) {
         __bf16* o = dq + (((int64_t)b * N + ip) * Hq + head) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -829,6 +832,7 @@ __device__ __forceinline__ void dq_item(const __bf16* __restrict__ q, const __bf
                 *reinterpret_cast<bf16x4*>(o + db * 32 + grp * 8 + hi * 4) = v4;
             }
     }
+    return true;
 }
 
 // Persistent dQ: one 512-thread workgroup per CU takes work items from NQ
@@ -852,44 +856,41 @@ __device__ __attribute__((noinline)) void plan_in_wg(const int32_t* tmax, const 
     make_plan<512>(tmax, tiso, B, N, T, G, Hkv, ctrl, tile_plan, units, split_tiles, lds);
 }
 
-// A dQ work item made of isolated slots only: P = 1 on the diagonal and
-// nothing else, so dS = dout.v - dout.out = 0 and dq = dk = 0; dv of a key is
-// the sum of the dout rows of the G query heads that share its KV head.  The
-// item writes dq = 0 for its BM positions x HB heads and, once per KV head
-// (the item of head chunk 0), dk and dv of its BM positions.  dK/dV and the
-// reduction of split tiles run later and rewrite the keys of tiles they own,
-// with the same values up to rounding.  Out of line, so that the main item's
-// registers are allocated without it.
-template <int D, int HB>
-__device__ __attribute__((noinline)) void dq_iso_item(const __bf16* __restrict__ dout,
-                                                      const int32_t* __restrict__ tiso, int B, int N, int Hq,
-                                                      int Hkv, int T, int n_qtiles, int n_chunks,
-                                                      __bf16* __restrict__ dq, __bf16* __restrict__ dk,
-                                                      __bf16* __restrict__ dv, int item) {
-    constexpr int BM = 256 / HB, LPR = D / 8, RPW = 64 / LPR;
-    const int GH = B * Hkv * n_chunks;
-    const int gi = item % GH, qt = n_qtiles - 1 - item / GH;
-    const int chunk = gi % n_chunks, g = (gi / n_chunks) % Hkv, b = gi / (n_chunks * Hkv);
-    const int G = Hq / Hkv;
-    const int i0 = qt * BM, t_last = (min(i0 + BM, N) - 1) / KT;
-    int iso = 1;
-    for (int t = i0 / KT; t <= t_last; ++t) iso &= tiso[(int64_t)b * T + t];
-    if (!iso) return;
+// One unit of isolated-slot work of the backward: part `unit % kIsoSplit` of
+// listed tile `unit / kIsoSplit`.  P = 1 on the diagonal and nothing else, so
+// dS = P (dP - delta) = dout.v - dout.out = 0: dq = dk = 0, and dv of a key is
+// the sum of the dout rows of the query heads sharing its KV head.  The dK/dV
+// kernel runs later and rewrites the keys of every 256-key tile it owns (the
+// same values up to rounding), so a key of an isolated 64-key tile inside a
+// mixed 256-key tile ends with its values.  Out of line, so that the main
+// item's registers are allocated without it.
+template <int D>
+__device__ __attribute__((noinline)) void dq_iso_unit(const __bf16* __restrict__ dout,
+                                                      const int32_t* __restrict__ iso_list, int N, int Hq, int Hkv,
+                                                      int T, __bf16* __restrict__ dq, __bf16* __restrict__ dk,
+                                                      __bf16* __restrict__ dv, int unit) {
+    constexpr int LPR = D / 8, RPW = 64 / LPR;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int G = Hq / Hkv;
     const int e = (lane % LPR) * 8;
     const bf16x8 z = {};
+    const int bt = iso_list[unit / kIsoSplit];
+    const int t = bt % T, b = bt / T;
+    const int part = unit % kIsoSplit;
+    const int qrows = KT * Hq / kIsoSplit, qbase = part * qrows;
 #pragma unroll 4
-    for (int r0 = wave * RPW; r0 < 256; r0 += 8 * RPW) {
+    for (int r0 = qbase + wave * RPW; r0 < qbase + qrows; r0 += 8 * RPW) {  // dq rows
         const int r = r0 + lane / LPR;
-        const int pos = i0 + r / HB, head = g * G + chunk * HB + r % HB;
-        if (pos < N) *reinterpret_cast<bf16x8*>(dq + (((int64_t)b * N + pos) * Hq + head) * D + e) = z;
+        const int slot = t * KT + r / Hq;
+        if (slot < N) *reinterpret_cast<bf16x8*>(dq + (((int64_t)b * N + slot) * Hq + r % Hq) * D + e) = z;
     }
-    if (chunk != 0) return;
-    for (int r0 = wave * RPW; r0 < BM; r0 += 8 * RPW) {
-        const int pos = i0 + r0 + lane / LPR;
-        if (pos >= N) continue;
+    const int kvrows = KT * Hkv / kIsoSplit, kvbase = part * kvrows;
+    for (int r0 = kvbase + wave * RPW; r0 < kvbase + kvrows; r0 += 8 * RPW) {  // dk, dv rows
+        const int r = r0 + lane / LPR;
+        const int slot = t * KT + r / Hkv, g = r % Hkv;
+        if (slot >= N) continue;
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        const __bf16* src = dout + (((int64_t)b * N + pos) * Hq + (int64_t)g * G) * D + e;
+        const __bf16* src = dout + (((int64_t)b * N + slot) * Hq + (int64_t)g * G) * D + e;
         for (int h = 0; h < G; ++h) {
             const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(src + (int64_t)h * D);
 #pragma unroll
@@ -898,7 +899,7 @@ __device__ __attribute__((noinline)) void dq_iso_item(const __bf16* __restrict__
         bf16x8 o;
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[i] = (__bf16)acc[i];
-        const int64_t kv = (((int64_t)b * N + pos) * Hkv + g) * D + e;
+        const int64_t kv = (((int64_t)b * N + slot) * Hkv + g) * D + e;
         *reinterpret_cast<bf16x8*>(dk + kv) = z;
         *reinterpret_cast<bf16x8*>(dv + kv) = o;
     }
@@ -915,7 +916,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
                                                  int B, int N, int Hq, int Hkv, int T, int n_qtiles, int n_chunks,
                                                  float scale_log2, float scale, __bf16* __restrict__ dq,
                                                  __bf16* __restrict__ dk, __bf16* __restrict__ dv,
-                                                 int* __restrict__ qctr, int NQ, int n_items, PlanArgs plan) {
+                                                 const int32_t* __restrict__ iso_list, int* __restrict__ qctr,
+                                                 int NQ, int n_items, PlanArgs plan) {
     constexpr int STAGE = 2 * KT * D * 2 + KT * 4;
     __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];
     __shared__ int list[1024];
@@ -930,16 +932,32 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
                    plan.units, plan.split_tiles, reinterpret_cast<int*>(smem));
         __syncthreads();
     }
+    const int n_units = qctr[kIsoCount] * kIsoSplit;  // isolated-slot units
+    auto claim = [&](int* ctr) {
+        if (threadIdx.x == 0) s_item = atomicAdd(ctr, 1);
+        __syncthreads();
+        const int x = __builtin_amdgcn_readfirstlane(s_item);
+        __syncthreads();
+        return x;
+    };
     for (;;) {
-        if (threadIdx.x == 0) s_item = qx + NQ * atomicAdd(&qctr[qx], 1);
-        __syncthreads();
-        const int item = __builtin_amdgcn_readfirstlane(s_item);
-        __syncthreads();
+        const int item = qx + NQ * claim(&qctr[qx]);
         if (item >= n_items) break;
-        dq_iso_item<D, HB>(dout, tiso, B, N, Hq, Hkv, T, n_qtiles, n_chunks, dq, dk, dv, item);
-        dq_item<D, HB>(q, k, v, out, dout, lse, delta, lse2, se, tmin, tmax, tiso, B, N, Hq, Hkv, T, n_qtiles,
-                       n_chunks, scale_log2, scale, dq, item, smem, list, list_meta);
+        const bool worked = dq_item<D, HB>(q, k, v, out, dout, lse, delta, lse2, se, tmin, tmax, tiso, B, N, Hq,
+                                           Hkv, T, n_qtiles, n_chunks, scale_log2, scale, dq, item, smem, list,
+                                           list_meta);
         __syncthreads();  // the stages and the list are reused by the next item
+        // one unit of the (HBM-bound) isolated-slot work after each item of
+        // matrix work, spread over the kernel as in the forward
+        if (worked) {
+            const int u = claim(&qctr[kIsoQueue]);
+            if (u < n_units) dq_iso_unit<D>(dout, iso_list, N, Hq, Hkv, T, dq, dk, dv, u);
+        }
+    }
+    for (;;) {  // what is left of it
+        const int u = claim(&qctr[kIsoQueue]);
+        if (u >= n_units) break;
+        dq_iso_unit<D>(dout, iso_list, N, Hq, Hkv, T, dq, dk, dv, u);
     }
 }
 
@@ -956,7 +974,7 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.out, (const __bf16*)a.dout, a.lse,
                        w.delta, w.lse2, a.se, w.tile_min, w.tile_max, w.tile_iso, a.B, a.N, a.Hq, a.Hkv, T,
                        n_qtiles, n_chunks, a.scale * kLog2e, a.scale, (__bf16*)a.dq, (__bf16*)a.dk, (__bf16*)a.dv,
-                       w.qctr, NQ, (int)items,
+                       w.iso_list, w.qctr, NQ, (int)items,
                        PlanArgs{w.tile_max, w.tile_iso, a.B, a.N, T, a.Hq / a.Hkv, a.Hkv, w.ctrl, w.tile_plan, w.units,
                                 w.split_tiles});
     return hipGetLastError();
@@ -965,7 +983,7 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
 template <int D>
 hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
-    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, w.tile_iso, w.qctr, st);
+    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, w.tile_iso, w.iso_list, w.qctr, st);
     if (e != hipSuccess) return e;
     // dQ first: it also writes delta and lse * log2(e), which dK/dV reads
     switch (heads_per_wg(a.Hq / a.Hkv)) {
@@ -1002,8 +1020,8 @@ size_t plan_bytes(int B, int N, int Hkv, int D) {
 
 size_t mfma_bwd_ws_bytes(int B, int N, int Hq, int Hkv, int D) {
     const size_t T = (size_t)(N + KT - 1) / KT;
-    return 2 * align256((size_t)B * Hq * N * sizeof(float)) + 3 * align256((size_t)B * T * sizeof(int32_t)) +
-           align256(kItemQueues * sizeof(int32_t)) + plan_bytes(B, N, Hkv, D);
+    return 2 * align256((size_t)B * Hq * N * sizeof(float)) + 4 * align256((size_t)B * T * sizeof(int32_t)) +
+           align256(kQueueCounters * sizeof(int32_t)) + plan_bytes(B, N, Hkv, D);
 }
 
 BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D) {
@@ -1020,8 +1038,10 @@ BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D) {
     p += align256((size_t)B * T * sizeof(int32_t));
     w.tile_iso = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)B * T * sizeof(int32_t));
+    w.iso_list = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)B * T * sizeof(int32_t));
     w.qctr = reinterpret_cast<int32_t*>(p);
-    p += align256(kItemQueues * sizeof(int32_t));
+    p += align256(kQueueCounters * sizeof(int32_t));
     const size_t TT = (size_t)(N + kKvTile - 1) / kKvTile;
     const size_t ucap = (size_t)kSplitSlots + (size_t)B * TT * Hkv;
     w.ctrl = reinterpret_cast<int32_t*>(p);

@@ -17,8 +17,9 @@
 //     keeps its Q fragments in registers;
 //   * the kernel is persistent: one workgroup per CU takes items from
 //     per-XCD queues, deepest query block first.
-// An item whose slots all see and are seen only by themselves (padding,
-// one-token sequences) gets the one-key result from fwd_iso_item instead.
+// Tiles whose slots all see and are seen only by themselves (padding,
+// one-token sequences) get the one-key result from isolated-slot units, one
+// of which a workgroup takes after each item of matrix work.
 // Products are v_mfma_f32_32x32x16_bf16 in the transposed orientation:
 //   S^T = K Q^T   (A = K from LDS, B = Q^T from registers)
 //   O^T += V^T P^T (A = V^T from LDS, B = P^T straight from the S^T accumulator)
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(256) void fwd_prep(const int32_t* __restrict__ se, 
                                                 int32_t* __restrict__ tmin, int32_t* __restrict__ tmax,
                                                 int32_t* __restrict__ tiso, int32_t* __restrict__ qctr) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6), b = blockIdx.y, lane = threadIdx.x & 63;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kItemQueues) qctr[threadIdx.x] = 0;  // work queues
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kQueueCounters) qctr[threadIdx.x] = 0;  // work queues
     if (t >= T) return;
     const int j = t * KT + lane;
     const int s = j < N ? se[(int64_t)b * N + j] : -1;
@@ -70,9 +71,14 @@ __global__ __launch_bounds__(256) void fwd_prep(const int32_t* __restrict__ se, 
 // only is isolated when no key before the tile reaches into it, i.e. the
 // largest subtree_end before the tile is below its first slot.  Grid (B), 1024
 // threads; a running maximum over the tiles, 1024 per step.
+// The isolated tiles are also listed (as b * T + t, in no particular order) in
+// iso_list, their number in qctr[kIsoCount].
 __global__ __launch_bounds__(1024) void iso_scan(const int32_t* __restrict__ tmax, int T,
-                                                 int32_t* __restrict__ tiso) {
+                                                 int32_t* __restrict__ tiso, int32_t* __restrict__ iso_list,
+                                                 int32_t* __restrict__ qctr) {
     __shared__ int s_wave[16];
+    __shared__ int s_cnt[16];
+    __shared__ int s_base;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int carry = -1;  // largest subtree_end of the tiles before this step's
     for (int c0 = 0; c0 < T; c0 += 1024) {
@@ -99,18 +105,75 @@ __global__ __launch_bounds__(1024) void iso_scan(const int32_t* __restrict__ tma
         const int incl = max(v, wave > 0 ? s_wave[wave - 1] : -1);
         const int prev = __shfl_up(incl, 1, 64);
         const int before = max(carry, lane > 0 ? prev : (wave > 0 ? s_wave[wave - 1] : -1));
+        int flag = 0;
         if (t < T) {
             int* f = tiso + (int64_t)b * T + t;
-            *f = (*f && before < t * KT) ? 1 : 0;
+            flag = (*f && before < t * KT) ? 1 : 0;
+            *f = flag;
         }
+        // append the isolated tiles of this step: rank inside the wave by a
+        // ballot, then wave offsets, one atomic per step for the base
+        const unsigned long long m = __ballot(flag);
+        if (lane == 0) s_cnt[wave] = __popcll(m);
         carry = max(carry, s_wave[15]);
         __syncthreads();
+        if (tid == 0) {
+            int run = 0;
+            for (int w = 0; w < 16; ++w) {
+                const int c = s_cnt[w];
+                s_cnt[w] = run;
+                run += c;
+            }
+            s_base = run ? atomicAdd(&qctr[kIsoCount], run) : 0;
+        }
+        __syncthreads();
+        if (flag) iso_list[s_base + s_cnt[wave] + __popcll(m & ((1ull << lane) - 1ull))] = b * T + t;
+        __syncthreads();
+    }
+}
+
+// One unit of isolated-slot work of the forward: part `unit % kIsoSplit` of
+// the (slot, head) rows of listed tile `unit / kIsoSplit`: a query that sees
+// only itself has a one-term softmax, so out = v and lse = scale q.k; D / 8
+// lanes per row.  Out of line, so that the main item's registers are
+// allocated without it.
+template <int D>
+__device__ __attribute__((noinline)) void fwd_iso_unit(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                       const __bf16* __restrict__ v,
+                                                       const int32_t* __restrict__ iso_list, int N, int Hq, int Hkv,
+                                                       int T, float scale, __bf16* __restrict__ out,
+                                                       float* __restrict__ lse, int unit) {
+    constexpr int LPR = D / 8, RPW = 64 / LPR;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int G = Hq / Hkv, rows = KT * Hq / kIsoSplit;
+    const int e = (lane % LPR) * 8;
+    const int bt = iso_list[unit / kIsoSplit];
+    const int t = bt % T, b = bt / T;
+    const int rbase = (unit % kIsoSplit) * rows;
+#pragma unroll 4
+    for (int r0 = rbase + wave * RPW; r0 < rbase + rows; r0 += 8 * RPW) {
+        const int r = r0 + lane / LPR;
+        const int slot = t * KT + r / Hq, h = r % Hq;
+        const int sc = min(slot, N - 1);
+        const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(q + (((int64_t)b * N + sc) * Hq + h) * D + e);
+        const int64_t kv = (((int64_t)b * N + sc) * Hkv + h / G) * D + e;
+        const bf16x8 k8 = *reinterpret_cast<const bf16x8*>(k + kv);
+        const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(v + kv);
+        float dot = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dot = fmaf((float)q8[i], (float)k8[i], dot);
+#pragma unroll
+        for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o, 64);
+        if (slot < N) {
+            *reinterpret_cast<bf16x8*>(out + (((int64_t)b * N + slot) * Hq + h) * D + e) = v8;
+            if (lane % LPR == 0) lse[((int64_t)b * Hq + h) * N + slot] = dot * scale;
+        }
     }
 }
 
 // One work item of the forward: BM positions x HB query heads of one KV head.
 template <int D, int HB>
-__device__ __forceinline__ void fwd_item(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+__device__ __forceinline__ bool fwd_item(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                          const __bf16* __restrict__ v, const int32_t* __restrict__ se,
                                          const int32_t* __restrict__ tmin, const int32_t* __restrict__ tmax,
                                          const int32_t* __restrict__ tiso, int B, int N, int Hq, int Hkv, int T,
@@ -145,10 +208,10 @@ __device__ __forceinline__ void fwd_item(const __bf16* __restrict__ q, const __b
     const int i_last = min(i0 + BM, N) - 1;
     const int t_last = i_last / KT;
     {
-        // a block of isolated slots only is written by fwd_iso_item
+        // a block of isolated slots only is left to the isolated-slot units
         int iso = 1;
         for (int t = i0 / KT; t <= t_last; ++t) iso &= tiso[(int64_t)b * T + t];
-        if (iso) return;
+        if (iso) return false;
     }
     const int32_t* tmaxb = tmax + (int64_t)b * T;
     const int32_t* tminb = tmin + (int64_t)b * T;
@@ -352,7 +415,8 @@ __device__ __forceinline__ void fwd_item(const __bf16* __restrict__ q, const __b
 
     // epilogue: O = O^T / l, lse = (m + log2 l) ln 2
     const float lt = add_xor32(l_run);
-    if (ip < N) {
+    // rows of isolated tiles belong to the isolated-slot units
+    if (ip < N && !tiso[(int64_t)b * T + ip / KT]) {
         const float inv = 1.f / lt;
         __bf16* o = out + (((int64_t)b * N + ip) * Hq + head) * D;
 #pragma unroll
@@ -366,48 +430,7 @@ __device__ __forceinline__ void fwd_item(const __bf16* __restrict__ q, const __b
             }
         if (hi == 0) lse[((int64_t)b * Hq + head) * N + ip] = (m_run + __log2f(lt)) * kLn2;
     }
-}
-
-// A forward work item made of isolated slots only: the one-term softmax,
-// out = v and lse = scale q.k, for its BM positions x HB query heads; 16 lanes
-// (D / 8) per (position, head) row.  Out of line, so that the main item's
-// registers are allocated without it.  Returns at once for other items.
-template <int D, int HB>
-__device__ __attribute__((noinline)) void fwd_iso_item(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                                                       const __bf16* __restrict__ v, const int32_t* __restrict__ tiso,
-                                                       int B, int N, int Hq, int Hkv, int T, int n_qtiles,
-                                                       int n_chunks, float scale, __bf16* __restrict__ out,
-                                                       float* __restrict__ lse, int item) {
-    constexpr int BM = 256 / HB, LPR = D / 8, RPW = 64 / LPR;
-    const int GH = B * Hkv * n_chunks;
-    const int gi = item % GH, qt = n_qtiles - 1 - item / GH;
-    const int chunk = gi % n_chunks, g = (gi / n_chunks) % Hkv, b = gi / (n_chunks * Hkv);
-    const int G = Hq / Hkv;
-    const int i0 = qt * BM, t_last = (min(i0 + BM, N) - 1) / KT;
-    int iso = 1;
-    for (int t = i0 / KT; t <= t_last; ++t) iso &= tiso[(int64_t)b * T + t];
-    if (!iso) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e = (lane % LPR) * 8;
-#pragma unroll 4
-    for (int r0 = wave * RPW; r0 < 256; r0 += 8 * RPW) {
-        const int r = r0 + lane / LPR;
-        const int pos = i0 + r / HB, head = g * G + chunk * HB + r % HB;
-        const int pc = min(pos, N - 1);
-        const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(q + (((int64_t)b * N + pc) * Hq + head) * D + e);
-        const int64_t kv = (((int64_t)b * N + pc) * Hkv + g) * D + e;
-        const bf16x8 k8 = *reinterpret_cast<const bf16x8*>(k + kv);
-        const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(v + kv);
-        float dot = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dot = fmaf((float)q8[i], (float)k8[i], dot);
-#pragma unroll
-        for (int o = 1; o < LPR; o <<= 1) dot += __shfl_xor(dot, o, 64);
-        if (pos < N) {
-            *reinterpret_cast<bf16x8*>(out + (((int64_t)b * N + pos) * Hq + head) * D + e) = v8;
-            if (lane % LPR == 0) lse[((int64_t)b * Hq + head) * N + pos] = dot * scale;
-        }
-    }
+    return true;
 }
 
 // Persistent forward: one 512-thread workgroup per CU takes work items from
@@ -423,23 +446,40 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
                                                    const int32_t* __restrict__ tiso, int B, int N, int Hq,
                                                    int Hkv, int T, int n_qtiles, int n_chunks, float scale_log2,
                                                    float scale, __bf16* __restrict__ out, float* __restrict__ lse,
-                                                   int* __restrict__ qctr, int NQ, int n_items) {
+                                                   const int32_t* __restrict__ iso_list, int* __restrict__ qctr,
+                                                   int NQ, int n_items) {
     constexpr int STAGE = 2 * KT * D * 2 + KT * 4;
     __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];
     __shared__ int list[1024];
     __shared__ int list_meta[2];
     __shared__ int s_item;
     const int qx = blockIdx.x % NQ;
+    const int n_units = qctr[kIsoCount] * kIsoSplit;  // isolated-slot units
+    auto claim = [&](int* ctr) {
+        if (threadIdx.x == 0) s_item = atomicAdd(ctr, 1);
+        __syncthreads();
+        const int x = __builtin_amdgcn_readfirstlane(s_item);
+        __syncthreads();
+        return x;
+    };
     for (;;) {
-        if (threadIdx.x == 0) s_item = qx + NQ * atomicAdd(&qctr[qx], 1);
-        __syncthreads();
-        const int item = __builtin_amdgcn_readfirstlane(s_item);
-        __syncthreads();
+        const int item = qx + NQ * claim(&qctr[qx]);
         if (item >= n_items) break;
-        fwd_iso_item<D, HB>(q, k, v, tiso, B, N, Hq, Hkv, T, n_qtiles, n_chunks, scale, out, lse, item);
-        fwd_item<D, HB>(q, k, v, se, tmin, tmax, tiso, B, N, Hq, Hkv, T, n_qtiles, n_chunks, scale_log2, out, lse,
-                        item, smem, list, list_meta);
+        const bool worked = fwd_item<D, HB>(q, k, v, se, tmin, tmax, tiso, B, N, Hq, Hkv, T, n_qtiles, n_chunks,
+                                            scale_log2, out, lse, item, smem, list, list_meta);
         __syncthreads();  // the stages and the list are reused by the next item
+        // one unit of the (HBM-bound) isolated-slot work after each item of
+        // matrix work, so that it is spread over the kernel instead of
+        // saturating HBM on every CU at once
+        if (worked) {
+            const int u = claim(&qctr[kIsoQueue]);
+            if (u < n_units) fwd_iso_unit<D>(q, k, v, iso_list, N, Hq, Hkv, T, scale, out, lse, u);
+        }
+    }
+    for (;;) {  // what is left of it
+        const int u = claim(&qctr[kIsoQueue]);
+        if (u >= n_units) break;
+        fwd_iso_unit<D>(q, k, v, iso_list, N, Hq, Hkv, T, scale, out, lse, u);
     }
 }
 
@@ -456,14 +496,14 @@ hipError_t launch_main(const AttnArgs& a, const FwdWorkspace& w, int T, hipStrea
     hipLaunchKernelGGL((fwd_main<D, HB>), dim3((unsigned)grid), dim3(512), 0, st, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, a.se, w.tile_min, w.tile_max, w.tile_iso, a.B,
                        a.N, a.Hq, a.Hkv, T, n_qtiles, n_chunks, scale_log2, a.scale, (__bf16*)a.out, a.lse,
-                       w.qctr, NQ, (int)items);
+                       w.iso_list, w.qctr, NQ, (int)items);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st) {
     const int T = (a.N + KT - 1) / KT;
-    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, w.tile_iso, w.qctr, st);
+    hipError_t e = launch_tile_ranges(a.se, a.B, a.N, w.tile_min, w.tile_max, w.tile_iso, w.iso_list, w.qctr, st);
     if (e != hipSuccess) return e;
     switch (heads_per_wg(a.Hq / a.Hkv)) {
         case 1: e = launch_main<D, 1>(a, w, T, st); break;
@@ -483,7 +523,7 @@ size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D) {
     (void)Hkv;
     (void)D;
     const size_t T = (size_t)(N + KT - 1) / KT;
-    return 3 * align256((size_t)B * T * sizeof(int32_t)) + align256(kItemQueues * sizeof(int32_t));
+    return 4 * align256((size_t)B * T * sizeof(int32_t)) + align256(kQueueCounters * sizeof(int32_t));
 }
 
 FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D) {
@@ -498,17 +538,19 @@ FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D) {
     p += align256((size_t)B * T * sizeof(int32_t));
     w.tile_iso = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)B * T * sizeof(int32_t));
+    w.iso_list = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)B * T * sizeof(int32_t));
     w.qctr = reinterpret_cast<int32_t*>(p);
     return w;
 }
 
 hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, int32_t* tmax, int32_t* tiso,
-                              int32_t* qctr, hipStream_t st) {
+                              int32_t* iso_list, int32_t* qctr, hipStream_t st) {
     const int T = (N + KT - 1) / KT;
     hipLaunchKernelGGL(fwd_prep, dim3((T + 3) / 4, B), dim3(256), 0, st, se, N, T, tmin, tmax, tiso, qctr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(iso_scan, dim3(B), dim3(1024), 0, st, tmax, T, tiso);
+    hipLaunchKernelGGL(iso_scan, dim3(B), dim3(1024), 0, st, tmax, T, tiso, iso_list, qctr);
     return hipGetLastError();
 }
 
