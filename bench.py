@@ -3,7 +3,7 @@
 
 A step is one pass of the whole path over one packed row:
   tree_pack_layout (host, into pinned buffers) -> async copy of pos_ids and
-  subtree_end -> tree_rope(q), tree_rope(k) -> tree_attn_fwd -> tree_attn_bwd.
+  subtree_end -> tree_rope_qk(q, k) -> tree_attn_fwd -> tree_attn_bwd.
 Inputs (q, k, v, dout) are resident in HBM before timing starts.
 
 Throughput is algorithmic: ancestor pairs per head = sum over real slots of
@@ -234,8 +234,7 @@ def bench_sweep(args):
         def step(ev=None):
             if ev:
                 ev[0].record()
-            lib.tree_rope(q, pos, w.theta)
-            lib.tree_rope(k, pos, w.theta)
+            lib.tree_rope_qk(q, k, pos, w.theta)
             lib.tree_attn_fwd(q, k, v, se, scale, out=out, lse=lse, ws=wsf)
             if ev:
                 ev[1].record()
@@ -506,8 +505,7 @@ def main():
         bf["ev"].record(stream)
         if timing:
             timing[0].record(stream)
-        lib.tree_rope(q, pos_d, w.theta)
-        lib.tree_rope(k, pos_d, w.theta)
+        lib.tree_rope_qk(q, k, pos_d, w.theta)
         if timing:
             timing[1].record(stream)
         lib.tree_attn_fwd(q, k, v, se_d, scale, out=out, lse=lse, ws=wsf)

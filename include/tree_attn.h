@@ -11,6 +11,7 @@
  *   tree_place_leaves    sequences of a trie -> fixed-length rows (host)
  *   tree_pack_layout     parent array -> DFS slots, depth, subtree end, token_index (host)
  *   tree_rope            rotary embedding at depth, in place (device)
+ *   tree_rope_qk         the same on q and k in one launch (device)
  *   tree_attn_fwd        masked attention forward (device)
  *   tree_attn_bwd        its exact gradient (device)
  *   tree_gdn_plan        DFS row -> chains, 64-token chunks, depth buckets (host)
@@ -204,15 +205,30 @@ tree_status tree_validate_subtree_end(const int32_t* subtree_end, int64_t n);
  * [DAG "Positions"]: positions are graph depth, so along every root-to-leaf
  * path neighbouring tokens are one position apart.  Rotate-half pairing:
  * dimensions i and i + D/2 rotate by pos * theta^(-2i/D), i < D/2.  Angles
- * and sines are taken in fp64 and the result is rounded once to `dt`.
- * Slots at depth 0 are the identity and are left untouched.
+ * are formed in fp64 (for fp32 storage the sines and the rotation too; for
+ * bf16 the sines of the fp64-reduced angle in fp32, errors near 1e-7) and
+ * the result is rounded once to `dt`.  Slots at depth 0 are the identity
+ * and are left untouched.
  *
  *   x        [B, N, H, D] of dtype dt, rotated in place
  *   pos_ids  [B, N] int32 (tree_pack_layout's pos_ids per row)
  *   theta    base (> 0), e.g. 10000
+ * Errors: TREE_ERR_INVALID_ARG (negative sizes, null pointers, bad dtype or
+ * theta), TREE_ERR_UNSUPPORTED (D other than 64 or 128), TREE_ERR_DEVICE.
  */
 tree_status tree_rope(tree_dtype dt, void* x, int64_t B, int64_t N, int64_t H, int64_t D,
                       const int32_t* pos_ids, float theta, void* stream);
+
+/*
+ * tree_rope_qk - tree_rope on q [B, N, Hq, D] and k [B, N, Hkv, D] in one
+ * launch (same dtype, head dim, positions and theta; each slot's sines are
+ * computed once for both).  The results are those of tree_rope(q) followed
+ * by tree_rope(k), bit for bit.  q and k must not overlap
+ * (TREE_ERR_INVALID_ARG when they are the same buffer); either head count
+ * may be 0.  Other errors as tree_rope.
+ */
+tree_status tree_rope_qk(tree_dtype dt, void* q, void* k, int64_t B, int64_t N, int64_t Hq, int64_t Hkv,
+                         int64_t D, const int32_t* pos_ids, float theta, void* stream);
 
 /*
  * tree_attn_workspace_bytes - device workspace tree_attn_fwd (bwd = 0) or

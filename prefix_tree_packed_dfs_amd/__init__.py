@@ -24,5 +24,6 @@ from ._lib import (  # noqa: F401
     tree_place_leaves,
     tree_pack_layout,
     tree_rope,
+    tree_rope_qk,
     tree_validate_subtree_end,
 )

@@ -63,6 +63,9 @@ lib.tree_validate_subtree_end.restype = C.c_int
 lib.tree_validate_subtree_end.argtypes = [_i32p, C.c_int64]
 lib.tree_rope.restype = C.c_int
 lib.tree_rope.argtypes = [C.c_int, _vp, C.c_int64, C.c_int64, C.c_int64, C.c_int64, _vp, C.c_float, _vp]
+lib.tree_rope_qk.restype = C.c_int
+lib.tree_rope_qk.argtypes = [C.c_int, _vp, _vp, C.c_int64, C.c_int64, C.c_int64, C.c_int64, C.c_int64, _vp, C.c_float,
+                             _vp]
 lib.tree_attn_workspace_bytes.restype = C.c_size_t
 lib.tree_attn_workspace_bytes.argtypes = [C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
                                           C.c_int]
@@ -87,7 +90,8 @@ lib.tree_mfma_peak.restype = C.c_int
 lib.tree_mfma_peak.argtypes = [C.c_int64, C.c_int64, _vp, C.POINTER(C.c_double), _vp]
 
 EXPORTED = ("tree_abi_version", "tree_status_string", "tree_last_error", "tree_build_trie",
-            "tree_place_leaves", "tree_pack_layout", "tree_validate_subtree_end", "tree_rope", "tree_attn_workspace_bytes",
+            "tree_place_leaves", "tree_pack_layout", "tree_validate_subtree_end", "tree_rope", "tree_rope_qk",
+            "tree_attn_workspace_bytes",
             "tree_attn_fwd", "tree_attn_bwd", "tree_gdn_plan", "tree_gdn_workspace_bytes", "tree_gdn_fwd",
             "tree_mfma_peak")
 
@@ -237,6 +241,22 @@ def tree_rope(x, pos_ids, theta: float = 10000.0):
     _check(lib.tree_rope(_dtype_code(x), _dev(x, "x"), B, N, H, D, _dev(pos_ids, "pos_ids"), float(theta),
                          _stream()))
     return x
+
+
+def tree_rope_qk(q, k, pos_ids, theta: float = 10000.0):
+    """Rotate q [B, N, Hq, D] and k [B, N, Hkv, D] in place at depth pos_ids [B, N] (int32), one launch."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, N, H, D]")
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, N, Hkv, D) or k.dtype != q.dtype:
+        raise ValueError("k must be [B, N, Hkv, D] with q's dtype")
+    if pos_ids.dtype != torch.int32 or tuple(pos_ids.shape) != (B, N):
+        raise ValueError("pos_ids must be int32 [B, N]")
+    _check(lib.tree_rope_qk(_dtype_code(q), _dev(q, "q"), _dev(k, "k"), B, N, Hq, Hkv, D, _dev(pos_ids, "pos_ids"),
+                            float(theta), _stream()))
+    return q, k
 
 
 def tree_attn_workspace_bytes(dtype_code: int, B, N, Hq, Hkv, D, bwd: bool) -> int:

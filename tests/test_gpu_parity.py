@@ -78,6 +78,45 @@ def test_rope_matches_oracle(dtype, D):
     assert np.array_equal(got[pos == 0], x_in[pos == 0])
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", [("bf16", 128, 16, 8), ("bf16", 64, 3, 1), ("f32", 128, 4, 2),
+                                            ("bf16", 128, 0, 2), ("bf16", 128, 2, 0)])
+def test_rope_qk_equals_rope_on_each(dtype, D, Hq, Hkv):
+    """tree_rope_qk is tree_rope(q) then tree_rope(k), bit for bit (tree_rope is pinned to the oracle above)."""
+    import torch
+
+    import prefix_tree_packed_dfs_amd as lib
+
+    log(f"case rope_qk dtype={dtype} D={D} Hq={Hq} Hkv={Hkv}")
+    rng = np.random.default_rng(D + 7 * Hq + Hkv)
+    N = 1500
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = torch.from_numpy(rng.standard_normal((1, N, Hq, D)).astype(np.float32)).to(tdt).cuda()
+    k = torch.from_numpy(rng.standard_normal((1, N, Hkv, D)).astype(np.float32)).to(tdt).cuda()
+    pos = rng.integers(0, 40000, size=N).astype(np.int32)
+    pos[:4] = [0, 1, 36863, 0]
+    pos_d = torch.from_numpy(pos).view(1, N).cuda()
+    q1, k1 = q.clone(), k.clone()
+    lib.tree_rope(q1, pos_d, 10000.0)
+    lib.tree_rope(k1, pos_d, 10000.0)
+    lib.tree_rope_qk(q, k, pos_d, 10000.0)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q1)
+    assert torch.equal(k, k1)
+
+
+@pytest.mark.gpu
+def test_rope_qk_rejects_aliased_q_and_k():
+    import torch
+
+    import prefix_tree_packed_dfs_amd as lib
+
+    x = torch.zeros((1, 8, 2, 64), dtype=torch.bfloat16, device="cuda")
+    pos = torch.zeros((1, 8), dtype=torch.int32, device="cuda")
+    with pytest.raises(lib.TreeAttnError):
+        lib.tree_rope_qk(x, x, pos, 10000.0)
+
+
 # ---------------------------------------------------------------------------
 # small trees, every element compared
 # ---------------------------------------------------------------------------

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert declared == set(lib.EXPORTED)
     for name in declared:
         assert hasattr(lib.lib, name), name
-    assert lib.lib.tree_abi_version() == 3
+    assert lib.lib.tree_abi_version() == 4
 
 
 def _random_sequences(rng, n, max_len, vocab):
