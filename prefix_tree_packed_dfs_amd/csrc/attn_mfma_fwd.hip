@@ -280,19 +280,34 @@ __device__ __forceinline__ bool fwd_item(const __bf16* __restrict__ q, const __b
         // visible tiles of this query block, in order, with their class
         if (wave == 0) {
             int cnt = 0, next = -1;
-            for (int base = resume; base <= t_last; base += 64) {
-                const int t = base + lane;
-                const bool vis = t <= t_last && tmaxb[t] >= i0;
-                const bool full = vis && (t * KT + KT - 1 <= i0) && tminb[t] >= i_last;
-                const unsigned long long m = __ballot(vis);
-                const int n_m = __popcll(m);
-                if (cnt + n_m > LCAP) {
-                    next = base;
-                    break;
+            // the tile bounds of LPF chunks of 64 tiles are loaded together,
+            // so the list costs one memory latency per LPF chunks
+            constexpr int LPF = 4;
+            for (int base0 = resume; base0 <= t_last && next < 0; base0 += 64 * LPF) {
+                int tmx[LPF], tmn[LPF];
+#pragma unroll
+                for (int c = 0; c < LPF; ++c) {
+                    const int t = min(base0 + 64 * c + lane, t_last);
+                    tmx[c] = tmaxb[t];
+                    tmn[c] = tminb[t];
                 }
-                const int pos = cnt + __popcll(m & ((1ull << lane) - 1ull));
-                if (vis) list[pos] = t | (full ? FULL : 0);
-                cnt += n_m;
+#pragma unroll
+                for (int c = 0; c < LPF; ++c) {
+                    const int base = base0 + 64 * c;
+                    if (base > t_last) break;
+                    const int t = base + lane;
+                    const bool vis = t <= t_last && tmx[c] >= i0;
+                    const bool full = vis && (t * KT + KT - 1 <= i0) && tmn[c] >= i_last;
+                    const unsigned long long m = __ballot(vis);
+                    const int n_m = __popcll(m);
+                    if (cnt + n_m > LCAP) {
+                        next = base;
+                        break;
+                    }
+                    const int pos = cnt + __popcll(m & ((1ull << lane) - 1ull));
+                    if (vis) list[pos] = t | (full ? FULL : 0);
+                    cnt += n_m;
+                }
             }
             if (lane == 0) {
                 list_meta[0] = cnt;
