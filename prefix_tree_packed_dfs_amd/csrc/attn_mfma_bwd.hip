@@ -52,8 +52,9 @@ __device__ __forceinline__ T ld16(const void* p) {
 // block of the largest subtree_end among its keys.  Keys of a long shared
 // prefix visit almost the whole row while keys near the leaves visit a few
 // blocks, so a tile whose range exceeds C blocks is cut at multiples of C
-// (absolute block positions, C = budget / G; the budget doubles until the
-// chunks fit the partial-sum slots).  Each KV head has its own queue (g mod
+// (absolute block positions, C = budget / G; the budget grows by a quarter
+// until the chunks fit the partial-sum slots, so it stays within 25% of the
+// smallest that fits).  Each KV head has its own queue (g mod
 // NQ, so one XCD keeps one head's data), ordered longest unit first so that
 // the CUs of an XCD run out of work together.  The order of units of equal
 // length is arbitrary; every unit's result is the same whatever the order.
@@ -137,7 +138,7 @@ __device__ void make_plan(const int32_t* __restrict__ tmax, const int32_t* __res
         const bool fits = (int64_t)s_sum * Hkv <= kSplitSlots;
         __syncthreads();
         if (fits) break;
-        if (tid == 0) s_budget *= 2;
+        if (tid == 0) s_budget += max(1, s_budget / 4);
         __syncthreads();
     }
     // chunks per tile; slots and split-tile indices by an exclusive scan in tile order
