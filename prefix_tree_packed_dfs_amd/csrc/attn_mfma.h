@@ -56,7 +56,7 @@ struct BwdWorkspace {
 // initial visit budget per chunk.
 constexpr int kKvTile = 256;
 constexpr int kSplitSlots = 1536 * 256 / kKvTile;
-constexpr int kVisitBudget = 256;
+constexpr int kVisitBudget = 320;
 
 // Smallest and largest subtree_end of every KT-key tile of each row ([B, T]),
 // and whether every slot of the tile is isolated; the isolated tiles listed
