@@ -375,8 +375,11 @@ __device__ __forceinline__ bool fwd_item(const __bf16* __restrict__ q, const __b
                         const int4 s4 = *reinterpret_cast<const int4*>(ses + jj);
                         const int sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-                        for (int e4 = 0; e4 < 4; ++e4)
-                            if (!(j0 + jj + e4 <= ip && ip <= sv[e4])) scur[x][gq * 4 + e4] = -INFINITY;
+                        for (int e4 = 0; e4 < 4; ++e4) {
+                            // a select, not a branch: both tests on every lane
+                            const bool vis = (j0 + jj + e4 <= ip) & (ip <= sv[e4]);
+                            scur[x][gq * 4 + e4] = vis ? scur[x][gq * 4 + e4] : -INFINITY;
+                        }
                     }
             }
             // online softmax; the running max is only raised (and the output
