@@ -934,6 +934,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
         __syncthreads();
     }
     const int n_units = qctr[kIsoCount] * kIsoSplit;  // isolated-slot units
+    bool iso_left = n_units > 0;
     auto claim = [&](int* ctr) {
         if (threadIdx.x == 0) s_item = atomicAdd(ctr, 1);
         __syncthreads();
@@ -950,12 +951,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
         __syncthreads();  // the stages and the list are reused by the next item
         // one unit of the (HBM-bound) isolated-slot work after each item of
         // matrix work, spread over the kernel as in the forward
-        if (worked) {
+        if (worked && iso_left) {
             const int u = claim(&qctr[kIsoQueue]);
             if (u < n_units) dq_iso_unit<D>(dout, iso_list, N, Hq, Hkv, T, dq, dk, dv, u);
+            else iso_left = false;  // the queue is empty: no more claims
         }
     }
-    for (;;) {  // what is left of it
+    while (iso_left) {  // what is left of it
         const int u = claim(&qctr[kIsoQueue]);
         if (u >= n_units) break;
         dq_iso_unit<D>(dout, iso_list, N, Hq, Hkv, T, dq, dk, dv, u);

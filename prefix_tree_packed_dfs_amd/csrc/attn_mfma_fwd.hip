@@ -473,6 +473,7 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
     __shared__ int s_item;
     const int qx = blockIdx.x % NQ;
     const int n_units = qctr[kIsoCount] * kIsoSplit;  // isolated-slot units
+    bool iso_left = n_units > 0;
     auto claim = [&](int* ctr) {
         if (threadIdx.x == 0) s_item = atomicAdd(ctr, 1);
         __syncthreads();
@@ -489,12 +490,13 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
         // one unit of the (HBM-bound) isolated-slot work after each item of
         // matrix work, so that it is spread over the kernel instead of
         // saturating HBM on every CU at once
-        if (worked) {
+        if (worked && iso_left) {
             const int u = claim(&qctr[kIsoQueue]);
             if (u < n_units) fwd_iso_unit<D>(q, k, v, iso_list, N, Hq, Hkv, T, scale, out, lse, u);
+            else iso_left = false;  // the queue is empty: no more claims
         }
     }
-    for (;;) {  // what is left of it
+    while (iso_left) {  // what is left of it
         const int u = claim(&qctr[kIsoQueue]);
         if (u >= n_units) break;
         fwd_iso_unit<D>(q, k, v, iso_list, N, Hq, Hkv, T, scale, out, lse, u);
