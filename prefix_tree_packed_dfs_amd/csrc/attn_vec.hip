@@ -171,54 +171,54 @@ __global__ __launch_bounds__(TB) void vec_dq(const T* __restrict__ q, const T* _
     }
 }
 
-// One thread per key row of KV head g; loops over the query heads of the
+// Four lanes per key row of KV head g (lane c of a key owns the dimensions
+// c, c + 4, ...; the dot products are summed over the four lanes by two
+// exchanges), 16 keys per 64-lane block; loops over the query heads of the
 // group and over the queries i in [j, subtree_end[j]] (exactly the queries
-// that see key j), staged 64 at a time.
+// that see key j), staged 64 at a time.  Splitting a row over lanes shortens
+// the serial chain of each lane four times and gives four times the blocks.
+constexpr int kVecLanes = 4;
+
 template <typename T, int D>
 __global__ __launch_bounds__(TB) void vec_dkdv(const T* __restrict__ q, const T* __restrict__ k,
                                                const T* __restrict__ v, const int32_t* __restrict__ se,
                                                const float* __restrict__ lse, const float* __restrict__ delta,
                                                const T* __restrict__ dout, int N, int Hq, int Hkv, float scale,
                                                T* __restrict__ dk, T* __restrict__ dv) {
+    constexpr int KPB = TB / kVecLanes, DL = D / kVecLanes;
     __shared__ float qs[TB][D];
     __shared__ float dos[TB][D];
-    __shared__ float kr[TB][D + 1];  // own key and value rows, padded against bank conflicts
-    __shared__ float vr[TB][D + 1];
     __shared__ float ls[TB], dls[TB];
-    const int b = blockIdx.z, g = blockIdx.y, j0 = blockIdx.x * TB, t = threadIdx.x;
-    const int j = j0 + t;
+    const int b = blockIdx.z, g = blockIdx.y, t = threadIdx.x;
+    const int c = t % kVecLanes;
+    const int j0 = blockIdx.x * KPB, j = j0 + t / kVecLanes;
     const int G = Hq / Hkv;
     const int32_t* ser = se + (int64_t)b * N;
     const int sej = j < N ? ser[j] : -1;
     const int q_end = wave_max_i32(sej);  // last query any key of the block serves
-    for (int e = t; e < TB * D; e += TB) {
-        const int r = e / D, c = e % D, jj = j0 + r;
-        float kv = 0.f, vv = 0.f;
-        if (jj < N) {
-            const int64_t off = (((int64_t)b * N + jj) * Hkv + g) * D + c;
-            kv = to_f32(k[off]);
-            vv = to_f32(v[off]);
-        }
-        kr[r][c] = kv;
-        vr[r][c] = vv;
-    }
-    float adk[D], adv[D];
+    float kr[DL], vr[DL], adk[DL], adv[DL];
+    {
+        const int64_t off = (((int64_t)b * N + min(j, N - 1)) * Hkv + g) * D + c;
 #pragma unroll
-    for (int d = 0; d < D; ++d) adk[d] = adv[d] = 0.f;
-    __syncthreads();
+        for (int x = 0; x < DL; ++x) {
+            kr[x] = to_f32(k[off + kVecLanes * x]);
+            vr[x] = to_f32(v[off + kVecLanes * x]);
+            adk[x] = adv[x] = 0.f;
+        }
+    }
     for (int hh = 0; hh < G; ++hh) {
         const int h = g * G + hh;
         for (int i0 = j0; i0 <= q_end; i0 += TB) {
             for (int e = t; e < TB * D; e += TB) {
-                const int r = e / D, c = e % D, ii = i0 + r;
+                const int r = e / D, cc = e % D, ii = i0 + r;
                 float qv = 0.f, dv_ = 0.f;
                 if (ii < N) {
-                    const int64_t off = (((int64_t)b * N + ii) * Hq + h) * D + c;
+                    const int64_t off = (((int64_t)b * N + ii) * Hq + h) * D + cc;
                     qv = to_f32(q[off]) * scale;
                     dv_ = to_f32(dout[off]);
                 }
-                qs[r][c] = qv;
-                dos[r][c] = dv_;
+                qs[r][cc] = qv;
+                dos[r][cc] = dv_;
             }
             {
                 const int ii = i0 + t;
@@ -230,19 +230,24 @@ __global__ __launch_bounds__(TB) void vec_dkdv(const T* __restrict__ q, const T*
                 const int rn = min(TB, N - i0);
                 for (int r = 0; r < rn; ++r) {
                     const int ii = i0 + r;
-                    if (ii < j || ii > sej) continue;
+                    if (ii < j || ii > sej) continue;  // the same for the four lanes of a key
                     float s = 0.f, dpv = 0.f;
 #pragma unroll
-                    for (int d = 0; d < D; ++d) {
-                        s = fmaf(qs[r][d], kr[t][d], s);
-                        dpv = fmaf(dos[r][d], vr[t][d], dpv);
+                    for (int x = 0; x < DL; ++x) {
+                        s = fmaf(qs[r][c + kVecLanes * x], kr[x], s);
+                        dpv = fmaf(dos[r][c + kVecLanes * x], vr[x], dpv);
+                    }
+#pragma unroll
+                    for (int o = 1; o < kVecLanes; o <<= 1) {
+                        s += __shfl_xor(s, o, 64);
+                        dpv += __shfl_xor(dpv, o, 64);
                     }
                     const float p = expf(s - ls[r]);
                     const float ds = p * (dpv - dls[r]);
 #pragma unroll
-                    for (int d = 0; d < D; ++d) {
-                        adv[d] = fmaf(p, dos[r][d], adv[d]);
-                        adk[d] = fmaf(ds, qs[r][d], adk[d]);  // q already carries the scale
+                    for (int x = 0; x < DL; ++x) {
+                        adv[x] = fmaf(p, dos[r][c + kVecLanes * x], adv[x]);
+                        adk[x] = fmaf(ds, qs[r][c + kVecLanes * x], adk[x]);  // q already carries the scale
                     }
                 }
             }
@@ -250,12 +255,12 @@ __global__ __launch_bounds__(TB) void vec_dkdv(const T* __restrict__ q, const T*
         }
     }
     if (j < N) {
-        T* okp = dk + (((int64_t)b * N + j) * Hkv + g) * D;
-        T* ovp = dv + (((int64_t)b * N + j) * Hkv + g) * D;
+        T* okp = dk + (((int64_t)b * N + j) * Hkv + g) * D + c;
+        T* ovp = dv + (((int64_t)b * N + j) * Hkv + g) * D + c;
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            okp[d] = from_f32<T>(adk[d]);
-            ovp[d] = from_f32<T>(adv[d]);
+        for (int x = 0; x < DL; ++x) {
+            okp[kVecLanes * x] = from_f32<T>(adk[x]);
+            ovp[kVecLanes * x] = from_f32<T>(adv[x]);
         }
     }
 }
@@ -275,7 +280,8 @@ hipError_t launch_bwd(const AttnArgs& a, float* delta, hipStream_t st) {
                        (const T*)a.out, (const T*)a.dout, rows, a.N, a.Hq, delta);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 gq((a.N + TB - 1) / TB, a.Hq, a.B), gk((a.N + TB - 1) / TB, a.Hkv, a.B), block(TB);
+    constexpr int KPB = TB / kVecLanes;
+    dim3 gq((a.N + TB - 1) / TB, a.Hq, a.B), gk((a.N + KPB - 1) / KPB, a.Hkv, a.B), block(TB);
     hipLaunchKernelGGL((vec_dq<T, D>), gq, block, 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.se,
                        a.lse, delta, (const T*)a.dout, a.N, a.Hq, a.Hkv, a.scale, (T*)a.dq);
     e = hipGetLastError();
