@@ -6,7 +6,7 @@
 // subtree_end is below the first query of the block has no visible pair and
 // is skipped whole.
 //
-// One thread owns one query row (forward, dq) or one key row (dk/dv); the
+// Four lanes own one query row (forward, dq) or one key row (dk/dv); the
 // other side of the product is staged in LDS 64 rows at a time.  fp32
 // accumulation and softmax throughout.  These kernels serve the fp32 dtype,
 // whose tolerance (1e-5 relative) the bf16 matrix-core path cannot meet.
@@ -19,26 +19,31 @@ namespace treeattn {
 
 namespace {
 
-constexpr int TB = 64;  // rows per block = keys per tile
+constexpr int TB = 64;  // threads per block = keys per staged tile
+// Lanes per query (forward, dq) or key (dk/dv) row: lane c owns the
+// dimensions c, c + 4, ...; dot products are summed over the four lanes by
+// two exchanges.  A quarter of the serial work per lane, four times the blocks.
+constexpr int kVecLanes = 4;
 
 template <typename T, int D>
 __global__ __launch_bounds__(TB) void vec_fwd(const T* __restrict__ q, const T* __restrict__ k,
                                               const T* __restrict__ v, const int32_t* __restrict__ se,
                                               int N, int Hq, int Hkv, float scale, T* __restrict__ out,
                                               float* __restrict__ lse) {
+    constexpr int QPB = TB / kVecLanes, DL = D / kVecLanes;
     __shared__ float ks[TB][D];
     __shared__ float vs[TB][D];
     __shared__ int ses[TB];
-    const int b = blockIdx.z, h = blockIdx.y, i0 = blockIdx.x * TB, t = threadIdx.x;
-    const int i = i0 + t;
+    const int b = blockIdx.z, h = blockIdx.y, i0 = blockIdx.x * QPB, t = threadIdx.x;
+    const int c = t % kVecLanes, i = i0 + t / kVecLanes;
     const int g = h / (Hq / Hkv);
-    const int i_last = min(i0 + TB, N) - 1;
-    float qr[D], o[D];
-    const T* qp = q + (((int64_t)b * N + min(i, N - 1)) * Hq + h) * D;
+    const int i_last = min(i0 + QPB, N) - 1;
+    float qr[DL], o[DL];
+    const T* qp = q + (((int64_t)b * N + min(i, N - 1)) * Hq + h) * D + c;
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        qr[d] = to_f32(qp[d]) * scale;
-        o[d] = 0.f;
+    for (int x = 0; x < DL; ++x) {
+        qr[x] = to_f32(qp[kVecLanes * x]) * scale;
+        o[x] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
     const int32_t* ser = se + (int64_t)b * N;
@@ -48,30 +53,32 @@ __global__ __launch_bounds__(TB) void vec_fwd(const T* __restrict__ q, const T* 
         if (wave_max_i32(sej) < i0) continue;  // no key of this tile is visible to the block
         ses[t] = sej;
         for (int e = t; e < TB * D; e += TB) {
-            const int r = e / D, c = e % D, jj = j0 + r;
+            const int r = e / D, cc = e % D, jj = j0 + r;
             float kv = 0.f, vv = 0.f;
             if (jj < N) {
-                const int64_t off = (((int64_t)b * N + jj) * Hkv + g) * D + c;
+                const int64_t off = (((int64_t)b * N + jj) * Hkv + g) * D + cc;
                 kv = to_f32(k[off]);
                 vv = to_f32(v[off]);
             }
-            ks[r][c] = kv;
-            vs[r][c] = vv;
+            ks[r][cc] = kv;
+            vs[r][cc] = vv;
         }
         __syncthreads();
         if (i < N) {
             const int jn = min(TB, N - j0);
             for (int r = 0; r < jn; ++r) {
                 const int jj = j0 + r;
-                if (jj > i || i > ses[r]) continue;
+                if (jj > i || i > ses[r]) continue;  // the same for the four lanes of a query
                 float s = 0.f;
 #pragma unroll
-                for (int d = 0; d < D; ++d) s = fmaf(qr[d], ks[r][d], s);
+                for (int x = 0; x < DL; ++x) s = fmaf(qr[x], ks[r][c + kVecLanes * x], s);
+#pragma unroll
+                for (int w = 1; w < kVecLanes; w <<= 1) s += __shfl_xor(s, w, 64);
                 const float mn = fmaxf(m, s);
                 const float corr = expf(m - mn), p = expf(s - mn);
                 l = l * corr + p;
 #pragma unroll
-                for (int d = 0; d < D; ++d) o[d] = fmaf(p, vs[r][d], o[d] * corr);
+                for (int x = 0; x < DL; ++x) o[x] = fmaf(p, vs[r][c + kVecLanes * x], o[x] * corr);
                 m = mn;
             }
         }
@@ -79,10 +86,10 @@ __global__ __launch_bounds__(TB) void vec_fwd(const T* __restrict__ q, const T* 
     }
     if (i < N) {
         const float inv = 1.f / l;
-        T* op = out + (((int64_t)b * N + i) * Hq + h) * D;
+        T* op = out + (((int64_t)b * N + i) * Hq + h) * D + c;
 #pragma unroll
-        for (int d = 0; d < D; ++d) op[d] = from_f32<T>(o[d] * inv);
-        lse[((int64_t)b * Hq + h) * N + i] = m + logf(l);
+        for (int x = 0; x < DL; ++x) op[kVecLanes * x] = from_f32<T>(o[x] * inv);
+        if (c == 0) lse[((int64_t)b * Hq + h) * N + i] = m + logf(l);
     }
 }
 
@@ -109,22 +116,23 @@ __global__ __launch_bounds__(TB) void vec_dq(const T* __restrict__ q, const T* _
                                              const float* __restrict__ lse, const float* __restrict__ delta,
                                              const T* __restrict__ dout, int N, int Hq, int Hkv, float scale,
                                              T* __restrict__ dq) {
+    constexpr int QPB = TB / kVecLanes, DL = D / kVecLanes;
     __shared__ float ks[TB][D];
     __shared__ float vs[TB][D];
     __shared__ int ses[TB];
-    const int b = blockIdx.z, h = blockIdx.y, i0 = blockIdx.x * TB, t = threadIdx.x;
-    const int i = i0 + t;
+    const int b = blockIdx.z, h = blockIdx.y, i0 = blockIdx.x * QPB, t = threadIdx.x;
+    const int c = t % kVecLanes, i = i0 + t / kVecLanes;
     const int g = h / (Hq / Hkv);
-    const int i_last = min(i0 + TB, N) - 1;
+    const int i_last = min(i0 + QPB, N) - 1;
     const int ic = min(i, N - 1);
-    float qr[D], dor[D], acc[D];
-    const T* qp = q + (((int64_t)b * N + ic) * Hq + h) * D;
-    const T* dp = dout + (((int64_t)b * N + ic) * Hq + h) * D;
+    float qr[DL], dor[DL], acc[DL];
+    const T* qp = q + (((int64_t)b * N + ic) * Hq + h) * D + c;
+    const T* dp = dout + (((int64_t)b * N + ic) * Hq + h) * D + c;
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        qr[d] = to_f32(qp[d]) * scale;
-        dor[d] = to_f32(dp[d]);
-        acc[d] = 0.f;
+    for (int x = 0; x < DL; ++x) {
+        qr[x] = to_f32(qp[kVecLanes * x]) * scale;
+        dor[x] = to_f32(dp[kVecLanes * x]);
+        acc[x] = 0.f;
     }
     const float li = lse[((int64_t)b * Hq + h) * N + ic];
     const float di = delta[((int64_t)b * Hq + h) * N + ic];
@@ -135,39 +143,44 @@ __global__ __launch_bounds__(TB) void vec_dq(const T* __restrict__ q, const T* _
         if (wave_max_i32(sej) < i0) continue;
         ses[t] = sej;
         for (int e = t; e < TB * D; e += TB) {
-            const int r = e / D, c = e % D, jj = j0 + r;
+            const int r = e / D, cc = e % D, jj = j0 + r;
             float kv = 0.f, vv = 0.f;
             if (jj < N) {
-                const int64_t off = (((int64_t)b * N + jj) * Hkv + g) * D + c;
+                const int64_t off = (((int64_t)b * N + jj) * Hkv + g) * D + cc;
                 kv = to_f32(k[off]);
                 vv = to_f32(v[off]);
             }
-            ks[r][c] = kv;
-            vs[r][c] = vv;
+            ks[r][cc] = kv;
+            vs[r][cc] = vv;
         }
         __syncthreads();
         if (i < N) {
             const int jn = min(TB, N - j0);
             for (int r = 0; r < jn; ++r) {
                 const int jj = j0 + r;
-                if (jj > i || i > ses[r]) continue;
+                if (jj > i || i > ses[r]) continue;  // the same for the four lanes of a query
                 float s = 0.f, dpv = 0.f;
 #pragma unroll
-                for (int d = 0; d < D; ++d) {
-                    s = fmaf(qr[d], ks[r][d], s);
-                    dpv = fmaf(dor[d], vs[r][d], dpv);
+                for (int x = 0; x < DL; ++x) {
+                    s = fmaf(qr[x], ks[r][c + kVecLanes * x], s);
+                    dpv = fmaf(dor[x], vs[r][c + kVecLanes * x], dpv);
+                }
+#pragma unroll
+                for (int w = 1; w < kVecLanes; w <<= 1) {
+                    s += __shfl_xor(s, w, 64);
+                    dpv += __shfl_xor(dpv, w, 64);
                 }
                 const float ds = expf(s - li) * (dpv - di);
 #pragma unroll
-                for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, ks[r][d], acc[d]);
+                for (int x = 0; x < DL; ++x) acc[x] = fmaf(ds, ks[r][c + kVecLanes * x], acc[x]);
             }
         }
         __syncthreads();
     }
     if (i < N) {
-        T* o = dq + (((int64_t)b * N + i) * Hq + h) * D;
+        T* o = dq + (((int64_t)b * N + i) * Hq + h) * D + c;
 #pragma unroll
-        for (int d = 0; d < D; ++d) o[d] = from_f32<T>(acc[d] * scale);
+        for (int x = 0; x < DL; ++x) o[kVecLanes * x] = from_f32<T>(acc[x] * scale);
     }
 }
 
@@ -177,8 +190,6 @@ __global__ __launch_bounds__(TB) void vec_dq(const T* __restrict__ q, const T* _
 // group and over the queries i in [j, subtree_end[j]] (exactly the queries
 // that see key j), staged 64 at a time.  Splitting a row over lanes shortens
 // the serial chain of each lane four times and gives four times the blocks.
-constexpr int kVecLanes = 4;
-
 template <typename T, int D>
 __global__ __launch_bounds__(TB) void vec_dkdv(const T* __restrict__ q, const T* __restrict__ k,
                                                const T* __restrict__ v, const int32_t* __restrict__ se,
@@ -267,7 +278,8 @@ __global__ __launch_bounds__(TB) void vec_dkdv(const T* __restrict__ q, const T*
 
 template <typename T, int D>
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t st) {
-    dim3 grid((a.N + TB - 1) / TB, a.Hq, a.B), block(TB);
+    constexpr int QPB = TB / kVecLanes;
+    dim3 grid((a.N + QPB - 1) / QPB, a.Hq, a.B), block(TB);
     hipLaunchKernelGGL((vec_fwd<T, D>), grid, block, 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                        a.se, a.N, a.Hq, a.Hkv, a.scale, (T*)a.out, a.lse);
     return hipGetLastError();
@@ -280,8 +292,8 @@ hipError_t launch_bwd(const AttnArgs& a, float* delta, hipStream_t st) {
                        (const T*)a.out, (const T*)a.dout, rows, a.N, a.Hq, delta);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    constexpr int KPB = TB / kVecLanes;
-    dim3 gq((a.N + TB - 1) / TB, a.Hq, a.B), gk((a.N + KPB - 1) / KPB, a.Hkv, a.B), block(TB);
+    constexpr int RPB = TB / kVecLanes;  // query (dq) or key (dk/dv) rows per block
+    dim3 gq((a.N + RPB - 1) / RPB, a.Hq, a.B), gk((a.N + RPB - 1) / RPB, a.Hkv, a.B), block(TB);
     hipLaunchKernelGGL((vec_dq<T, D>), gq, block, 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.se,
                        a.lse, delta, (const T*)a.dout, a.N, a.Hq, a.Hkv, a.scale, (T*)a.dq);
     e = hipGetLastError();

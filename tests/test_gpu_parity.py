@@ -139,7 +139,8 @@ def test_random_tree_bf16_no_rope_and_rope(rope):
     _run_full(w, rope=rope, label=f"random_tree_bf16_rope={rope}")
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(2, 2, 64), (4, 1, 64), (8, 1, 128), (16, 2, 128), (32, 2, 64), (3, 3, 128)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(2, 2, 64), (4, 1, 64), (8, 1, 128), (16, 2, 128), (32, 2, 64), (3, 3, 128),
+                                     (6, 2, 64), (6, 2, 128)])
 def test_random_tree_bf16_head_shapes(Hq, Hkv, D):
     """Every GQA grouping the matrix-core kernels specialise (1, 4, 8 heads per KV head, and 16 as two
     workgroups of 8), head dim 64, and a ratio they do not cover (3 KV heads of 1), which runs on the
