@@ -6,8 +6,8 @@
 // subtree_end is below the first query of the block has no visible pair and
 // is skipped whole.
 //
-// Four lanes own one query row (forward, dq) or one key row (dk/dv); the
-// other side of the product is staged in LDS 64 rows at a time.  fp32
+// kVecLanes lanes own one query row (forward, dq) or one key row (dk/dv);
+// the other side of the product is staged in LDS 64 rows at a time.  fp32
 // accumulation and softmax throughout.  These kernels serve the fp32 dtype,
 // whose tolerance (1e-5 relative) the bf16 matrix-core path cannot meet.
 #include "attn_vec.h"
@@ -21,9 +21,10 @@ namespace {
 
 constexpr int TB = 64;  // threads per block = keys per staged tile
 // Lanes per query (forward, dq) or key (dk/dv) row: lane c owns the
-// dimensions c, c + 4, ...; dot products are summed over the four lanes by
-// two exchanges.  A quarter of the serial work per lane, four times the blocks.
-constexpr int kVecLanes = 4;
+// dimensions c, c + kVecLanes, ...; dot products are summed over the row's
+// lanes by log2(kVecLanes) exchanges.  An eighth of the serial work per lane
+// and eight times the blocks of one lane per row (16 lanes measured the same).
+constexpr int kVecLanes = 8;
 
 template <typename T, int D>
 __global__ __launch_bounds__(TB) void vec_fwd(const T* __restrict__ q, const T* __restrict__ k,
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(TB) void vec_fwd(const T* __restrict__ q, const T* 
             const int jn = min(TB, N - j0);
             for (int r = 0; r < jn; ++r) {
                 const int jj = j0 + r;
-                if (jj > i || i > ses[r]) continue;  // the same for the four lanes of a query
+                if (jj > i || i > ses[r]) continue;  // the same for every lane of a query
                 float s = 0.f;
 #pragma unroll
                 for (int x = 0; x < DL; ++x) s = fmaf(qr[x], ks[r][c + kVecLanes * x], s);
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(TB) void vec_dq(const T* __restrict__ q, const T* _
             const int jn = min(TB, N - j0);
             for (int r = 0; r < jn; ++r) {
                 const int jj = j0 + r;
-                if (jj > i || i > ses[r]) continue;  // the same for the four lanes of a query
+                if (jj > i || i > ses[r]) continue;  // the same for every lane of a query
                 float s = 0.f, dpv = 0.f;
 #pragma unroll
                 for (int x = 0; x < DL; ++x) {
@@ -184,12 +185,10 @@ __global__ __launch_bounds__(TB) void vec_dq(const T* __restrict__ q, const T* _
     }
 }
 
-// Four lanes per key row of KV head g (lane c of a key owns the dimensions
-// c, c + 4, ...; the dot products are summed over the four lanes by two
-// exchanges), 16 keys per 64-lane block; loops over the query heads of the
-// group and over the queries i in [j, subtree_end[j]] (exactly the queries
-// that see key j), staged 64 at a time.  Splitting a row over lanes shortens
-// the serial chain of each lane four times and gives four times the blocks.
+// kVecLanes lanes per key row of KV head g, 64 / kVecLanes keys per block;
+// loops over the query heads of the group and over the queries i in
+// [j, subtree_end[j]] (exactly the queries that see key j), staged 64 at a
+// time.
 template <typename T, int D>
 __global__ __launch_bounds__(TB) void vec_dkdv(const T* __restrict__ q, const T* __restrict__ k,
                                                const T* __restrict__ v, const int32_t* __restrict__ se,
@@ -241,7 +240,7 @@ __global__ __launch_bounds__(TB) void vec_dkdv(const T* __restrict__ q, const T*
                 const int rn = min(TB, N - i0);
                 for (int r = 0; r < rn; ++r) {
                     const int ii = i0 + r;
-                    if (ii < j || ii > sej) continue;  // the same for the four lanes of a key
+                    if (ii < j || ii > sej) continue;  // the same for every lane of a key
                     float s = 0.f, dpv = 0.f;
 #pragma unroll
                     for (int x = 0; x < DL; ++x) {
