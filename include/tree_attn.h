@@ -31,7 +31,8 @@
  *   - The caller owns and allocates every buffer.  Host entry points take
  *     host pointers; device entry points take device pointers and enqueue
  *     asynchronously on `stream` (a hipStream_t; NULL = the default stream).
- *     The library keeps no state between calls and is thread-safe.
+ *     The library keeps no state between calls (beyond a per-device count of
+ *     compute units, read once) and is thread-safe.
  *   - Device tensors are contiguous:
  *       q, out, dout, dq : [B, N, Hq, D]      k, v, dk, dv : [B, N, Hkv, D]
  *       lse              : [B, Hq, N] fp32, natural log
@@ -192,10 +193,14 @@ tree_status tree_pack_layout(int32_t n_nodes, const int32_t* parent, int32_t n_s
 
 /*
  * tree_validate_subtree_end - check a subtree_end row (host, synchronous).
- * TREE_OK iff j <= subtree_end[j] < n for every j and the intervals
- * [j, subtree_end[j]] are nested or disjoint (a valid pre-order interval
- * set).  The device entry points trust their subtree_end; call this on
- * input that did not come from tree_pack_layout().
+ *
+ * [ART "Token-mixing layers"]: in a depth-first layout a node's subtree is
+ * the contiguous run from its pre-order position to its exit position, so
+ * the intervals [j, subtree_end[j]] of a tree are nested or disjoint.
+ * TREE_OK iff j <= subtree_end[j] < n for every j and the intervals are
+ * nested or disjoint; TREE_ERR_BAD_TREE otherwise.  The device entry points
+ * trust their subtree_end; call this on input that did not come from
+ * tree_pack_layout().
  */
 tree_status tree_validate_subtree_end(const int32_t* subtree_end, int64_t n);
 
@@ -232,13 +237,36 @@ tree_status tree_rope_qk(tree_dtype dt, void* q, void* k, int64_t B, int64_t N, 
 
 /*
  * tree_attn_workspace_bytes - device workspace tree_attn_fwd (bwd = 0) or
- * tree_attn_bwd (bwd = 1) needs for these sizes.  Returns 0 on bad sizes.
- * The workspace holds per-call tables and work-queue counters that each call
- * re-initialises on its stream: calls that may run at the same time on the
- * GPU need workspaces of their own.
+ * tree_attn_bwd (bwd = 1) needs for these sizes, whatever the tree.  Returns
+ * 0 on bad sizes.  The workspace holds per-call tables and work-queue
+ * counters that each call re-initialises on its stream: calls that may run at
+ * the same time on the GPU need workspaces of their own.
+ *
+ * For the backward this is the largest workspace a call can use: a fixed
+ * part (delta, lse, tile tables, the dK/dV work plan) plus the most fp32
+ * partial-sum slots the plan ever takes (1,536 slots of 256 keys x D x 2;
+ * 384 MiB at D = 128).  The plan cuts key tiles whose visible query range is
+ * long into chunks that write partial sums; tree_attn_bwd() takes as many
+ * slots as the workspace it is given holds beyond the fixed part (down to
+ * none, when no tile is cut), and tree_attn_bwd_workspace_bytes_for() gives
+ * the exact size a row's plan uses.
  */
 size_t tree_attn_workspace_bytes(tree_dtype dt, int64_t B, int64_t N, int64_t Hq, int64_t Hkv,
                                  int64_t D, int bwd);
+
+/*
+ * tree_attn_bwd_workspace_bytes_for - backward workspace these rows' dK/dV
+ * plan uses (host, synchronous): the fixed part plus the partial-sum slots the
+ * plan takes at its first chunk budget (at most the 1,536 of
+ * tree_attn_workspace_bytes).  With at least this much, tree_attn_bwd() runs
+ * the same plan as with the largest workspace (bitwise the same results).
+ *
+ *   subtree_end  [B, N] int32 in HOST memory (the rows tree_attn_bwd() will get)
+ * Returns 0 on bad sizes or a NULL subtree_end with B * N > 0.  For shapes the
+ * vector path serves it returns its fixed workspace.
+ */
+size_t tree_attn_bwd_workspace_bytes_for(tree_dtype dt, const int32_t* subtree_end, int64_t B, int64_t N,
+                                         int64_t Hq, int64_t Hkv, int64_t D);
 
 /*
  * tree_attn_fwd - attention forward over packed rows (device).
@@ -254,7 +282,8 @@ size_t tree_attn_workspace_bytes(tree_dtype dt, int64_t B, int64_t N, int64_t Hq
  *   dt           TREE_BF16 (MFMA, fp32 accumulation and softmax) or TREE_F32
  *   q, k, v      inputs in dt (see layouts above); typically after tree_rope
  *   subtree_end  [B, N] int32 from tree_pack_layout (not checked on device)
- *   softmax_scale  usually 1/sqrt(D)
+ *   softmax_scale  usually 1/sqrt(D); finite and > 0, else TREE_ERR_INVALID_ARG
+ *                (the matrix-core path masks scores before scaling them)
  *   out          out [B, N, Hq, D] in dt
  *   lse          out [B, Hq, N] fp32
  *   ws, ws_bytes device workspace of at least tree_attn_workspace_bytes(dt, ..., 0) bytes
@@ -276,10 +305,15 @@ tree_status tree_attn_fwd(tree_dtype dt, const void* q, const void* k, const voi
  * dk and dv sum over the query heads that share a KV head.
  *
  *   out, lse     the forward's outputs for these inputs
+ *   softmax_scale  the forward's; finite and > 0, else TREE_ERR_INVALID_ARG
  *   dout         [B, N, Hq, D] in dt
  *   dq           out [B, N, Hq, D] in dt
  *   dk, dv       out [B, N, Hkv, D] in dt
- *   ws, ws_bytes device workspace of at least tree_attn_workspace_bytes(dt, ..., 1) bytes
+ *   ws, ws_bytes device workspace: tree_attn_bwd_workspace_bytes_for() of these rows
+ *                (or tree_attn_workspace_bytes(dt, ..., 1), which fits any rows).  Less
+ *                is accepted down to the fixed part (the size for rows without cut
+ *                tiles); the plan then cuts long key tiles into fewer chunks (same
+ *                results up to the order of summation).  Below that: TREE_ERR_CAPACITY.
  */
 tree_status tree_attn_bwd(tree_dtype dt, const void* q, const void* k, const void* v,
                           const int32_t* subtree_end, const void* out, const float* lse,

@@ -118,7 +118,7 @@ def slot_owners(token_index, n_nodes):
 
 def tree_attention(sequences, fid, dkey, tables, *, theta: Optional[float], min_shared: int = 64,
                    row_len: Optional[int] = None, backward: bool = True, scale: Optional[float] = None,
-                   q_slots=None, k_slots=None, storage: Optional[str] = None) -> TreeResult:
+                   q_slots=None, k_slots=None, storage: Optional[str] = None, kv_heads=None) -> TreeResult:
     """The whole oracle path: trie, layout, RoPE at depth, per-sequence attention, map back.
 
     ``tables`` holds q [n_feat,Hq,D], k/v [n_feat,Hkv,D] and do [n_dkey,Hq,D];
@@ -127,7 +127,9 @@ def tree_attention(sequences, fid, dkey, tables, *, theta: Optional[float], min_
     ``k_slots`` restrict the work to what out/lse/dq at ``q_slots`` and
     dk/dv at ``k_slots`` need (each of those outputs is still exact).
     ``theta`` None applies no rotary embedding.  ``storage`` ("f32" or "bf16") rounds the rotated q and k once to the
-    dtype of the tensors that hold them; everything else stays fp64.
+    dtype of the tensors that hold them; everything else stays fp64.  ``kv_heads`` (a list of KV heads)
+    computes only those heads and the query heads that read them (whole GQA groups, so dk/dv of those
+    heads are complete); the other heads' outputs are NaN.
     """
     trie = build_trie(sequences, min_shared=min_shared)
     n = trie.n_nodes
@@ -137,6 +139,9 @@ def tree_attention(sequences, fid, dkey, tables, *, theta: Optional[float], min_
     qt, kt, vt = tables["q"], tables["k"], tables["v"]
     Hq, D = qt.shape[1], qt.shape[2]
     Hkv = kt.shape[1]
+    G = Hq // Hkv
+    kvh = np.arange(Hkv) if kv_heads is None else np.asarray(sorted(set(int(g) for g in kv_heads)), dtype=np.int64)
+    qh = (kvh[:, None] * G + np.arange(G)[None, :]).ravel()   # the query heads of those groups
     scale = 1.0 / np.sqrt(D) if scale is None else scale
     R = layout.row_len
     sampled = q_slots is not None or k_slots is not None
@@ -160,12 +165,12 @@ def tree_attention(sequences, fid, dkey, tables, *, theta: Optional[float], min_
         slots = ti[s]
         pos = np.arange(L)
         if theta is None:                      # no rotary embedding
-            Qs = np.asarray(qt[fid[s]], dtype=np.float64)
-            Ks = np.asarray(kt[fid[s]], dtype=np.float64)
+            Qs = np.asarray(qt[fid[s]][:, qh], dtype=np.float64)
+            Ks = np.asarray(kt[fid[s]][:, kvh], dtype=np.float64)
         else:
-            Qs = round_to(rope(qt[fid[s]], pos, theta), storage)
-            Ks = round_to(rope(kt[fid[s]], pos, theta), storage)
-        Vs = np.asarray(vt[fid[s]], dtype=np.float64)
+            Qs = round_to(rope(qt[fid[s]][:, qh], pos, theta), storage)
+            Ks = round_to(rope(kt[fid[s]][:, kvh], pos, theta), storage)
+        Vs = np.asarray(vt[fid[s]][:, kvh], dtype=np.float64)
         owned = owner[slots] == s
         if sampled:
             fwd_rows = np.nonzero(owned & want_q[slots])[0]
@@ -174,16 +179,16 @@ def tree_attention(sequences, fid, dkey, tables, *, theta: Optional[float], min_
         if len(fwd_rows):
             O, l = causal_forward(Qs, Ks, Vs, scale, fwd_rows)
             dst = slots[fwd_rows]
-            done = ~np.isnan(out[dst, 0, 0])
+            done = ~np.isnan(out[dst, qh[0], 0])
             if np.any(done):
-                gap = max(gap, float(np.max(np.abs(out[dst[done]] - O[done]))),
-                          float(np.max(np.abs(lse[:, dst[done]] - l[:, done]))))
-            out[dst] = O
-            lse[:, dst] = l
+                gap = max(gap, float(np.max(np.abs(out[dst[done]][:, qh] - O[done]))),
+                          float(np.max(np.abs(lse[qh][:, dst[done]] - l[:, done]))))
+            out[dst[:, None], qh[None, :]] = O
+            lse[qh[:, None], dst[None, :]] = l
         if not backward:
             continue
-        dOs = np.zeros((L, Hq, D))
-        dOs[owned] = tables["do"][dkey[s][owned]]
+        dOs = np.zeros((L, len(qh), D))
+        dOs[owned] = tables["do"][dkey[s][owned]][:, qh]
         if sampled:
             kpos = np.nonzero(want_k[slots])[0]
             kmin = int(kpos.min()) if len(kpos) else L
@@ -195,9 +200,17 @@ def tree_attention(sequences, fid, dkey, tables, *, theta: Optional[float], min_
             continue
         dQ, dK, dV = causal_backward(Qs, Ks, Vs, dOs, scale, bwd_rows)
         own_rows = owned[bwd_rows]
-        dq[slots[bwd_rows[own_rows]]] = dQ[own_rows]
-        np.add.at(dk, slots, dK)
-        np.add.at(dv, slots, dV)
+        dq[slots[bwd_rows[own_rows]][:, None], qh[None, :]] = dQ[own_rows]
+        dk_s = np.zeros((L, Hkv, D))
+        dv_s = np.zeros((L, Hkv, D))
+        dk_s[:, kvh] = dK
+        dv_s[:, kvh] = dV
+        np.add.at(dk, slots, dk_s)
+        np.add.at(dv, slots, dv_s)
+    if backward and kv_heads is not None:
+        other = np.setdiff1d(np.arange(Hkv), kvh)
+        dk[:, other] = np.nan
+        dv[:, other] = np.nan
     if backward and sampled:
         keep = np.zeros(R, dtype=bool)
         keep[np.asarray(k_slots if k_slots is not None else [], dtype=np.int64)] = True

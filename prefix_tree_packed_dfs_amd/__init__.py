@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     tree_attn_bwd,
     tree_attn_fwd,
     tree_attn_workspace_bytes,
+    tree_attn_bwd_workspace_bytes_for,
     tree_build_trie,
     tree_gdn_fwd,
     tree_gdn_plan,

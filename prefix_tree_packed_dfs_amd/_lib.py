@@ -69,6 +69,9 @@ lib.tree_rope_qk.argtypes = [C.c_int, _vp, _vp, C.c_int64, C.c_int64, C.c_int64,
 lib.tree_attn_workspace_bytes.restype = C.c_size_t
 lib.tree_attn_workspace_bytes.argtypes = [C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
                                           C.c_int]
+lib.tree_attn_bwd_workspace_bytes_for.restype = C.c_size_t
+lib.tree_attn_bwd_workspace_bytes_for.argtypes = [C.c_int, _i32p, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
+                                                  C.c_int64]
 lib.tree_attn_fwd.restype = C.c_int
 lib.tree_attn_fwd.argtypes = [C.c_int, _vp, _vp, _vp, _vp, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
                               C.c_int64, C.c_float, _vp, _vp, _vp, C.c_size_t, _vp]
@@ -91,7 +94,7 @@ lib.tree_mfma_peak.argtypes = [C.c_int64, C.c_int64, _vp, C.POINTER(C.c_double),
 
 EXPORTED = ("tree_abi_version", "tree_status_string", "tree_last_error", "tree_build_trie",
             "tree_place_leaves", "tree_pack_layout", "tree_validate_subtree_end", "tree_rope", "tree_rope_qk",
-            "tree_attn_workspace_bytes",
+            "tree_attn_workspace_bytes", "tree_attn_bwd_workspace_bytes_for",
             "tree_attn_fwd", "tree_attn_bwd", "tree_gdn_plan", "tree_gdn_workspace_bytes", "tree_gdn_fwd",
             "tree_mfma_peak")
 
@@ -218,6 +221,18 @@ def _dev(t, name):
     return t.data_ptr()
 
 
+def _out(t, name, shape, dtype, like=None):
+    """A caller-supplied output buffer: right shape and dtype, or ValueError before any launch
+    (the kernels write the full extent the sizes imply)."""
+    if t is None:
+        return None
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {list(shape)}, got {t.dtype} {list(t.shape)}")
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{name} must be on {like.device}")
+    return t
+
+
 def _stream():
     torch = _torch()
     return torch.cuda.current_stream().cuda_stream
@@ -263,6 +278,16 @@ def tree_attn_workspace_bytes(dtype_code: int, B, N, Hq, Hkv, D, bwd: bool) -> i
     return int(lib.tree_attn_workspace_bytes(int(dtype_code), B, N, Hq, Hkv, D, 1 if bwd else 0))
 
 
+def tree_attn_bwd_workspace_bytes_for(dtype_code: int, subtree_end, Hq, Hkv, D) -> int:
+    """Backward workspace the dK/dV plan of these rows uses; subtree_end [B, N] (or [N]) int32 on the host."""
+    se = np.ascontiguousarray(subtree_end, dtype=np.int32)
+    if se.ndim == 1:
+        se = se[None]
+    B, N = se.shape
+    return int(lib.tree_attn_bwd_workspace_bytes_for(int(dtype_code), _ptr(se if se.size else np.zeros(1, np.int32),
+                                                                           C.c_int32), B, N, Hq, Hkv, D))
+
+
 def _shapes(q, k, v, subtree_end):
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -294,6 +319,8 @@ def tree_attn_fwd(q, k, v, subtree_end, softmax_scale=None, out=None, lse=None, 
     B, N, Hq, Hkv, D = _shapes(q, k, v, subtree_end)
     dt = _dtype_code(q)
     scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
+    out = _out(out, "out", q.shape, q.dtype, q)
+    lse = _out(lse, "lse", (B, Hq, N), torch.float32, q)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -316,9 +343,9 @@ def tree_attn_bwd(q, k, v, subtree_end, out, lse, dout, softmax_scale=None, dq=N
             raise ValueError(f"{nm} must match q")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N):
         raise ValueError("lse must be fp32 [B, Hq, N]")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty_like(q) if dq is None else _out(dq, "dq", q.shape, q.dtype, q)
+    dk = torch.empty_like(k) if dk is None else _out(dk, "dk", k.shape, k.dtype, q)
+    dv = torch.empty_like(v) if dv is None else _out(dv, "dv", v.shape, v.dtype, q)
     ws = _workspace(dt, B, N, Hq, Hkv, D, True, ws, q.device)
     _check(lib.tree_attn_bwd(dt, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(subtree_end, "subtree_end"),
                              _dev(out, "out"), _dev(lse, "lse"), _dev(dout, "dout"), B, N, Hq, Hkv, D, scale,

@@ -36,8 +36,9 @@ size_t fwd_ws(tree_dtype dt, int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int6
     return use_mfma(dt, Hq, Hkv, D) ? mfma_fwd_ws_bytes((int)B, (int)N, (int)Hkv, (int)D) : 0;
 }
 
-size_t bwd_ws(tree_dtype dt, int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t D) {
-    if (use_mfma(dt, Hq, Hkv, D)) return mfma_bwd_ws_bytes((int)B, (int)N, (int)Hq, (int)Hkv, (int)D);
+// Backward workspace with `slots` partial-sum slots (the vector path needs only delta).
+size_t bwd_ws(tree_dtype dt, int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t D, int slots) {
+    if (use_mfma(dt, Hq, Hkv, D)) return mfma_bwd_ws_bytes((int)B, (int)N, (int)Hq, (int)Hkv, (int)D, slots);
     return align_up((size_t)B * Hq * N * sizeof(float));  // delta
 }
 
@@ -51,7 +52,16 @@ tree_status device_status(hipError_t e, const char* what) {
 extern "C" size_t tree_attn_workspace_bytes(tree_dtype dt, int64_t B, int64_t N, int64_t Hq, int64_t Hkv,
                                             int64_t D, int bwd) {
     if (check_shapes(dt, B, N, Hq, Hkv, D) != TREE_OK) return 0;
-    return bwd ? bwd_ws(dt, B, N, Hq, Hkv, D) : fwd_ws(dt, B, N, Hq, Hkv, D);
+    return bwd ? bwd_ws(dt, B, N, Hq, Hkv, D, kSplitSlots) : fwd_ws(dt, B, N, Hq, Hkv, D);
+}
+
+extern "C" size_t tree_attn_bwd_workspace_bytes_for(tree_dtype dt, const int32_t* subtree_end, int64_t B,
+                                                    int64_t N, int64_t Hq, int64_t Hkv, int64_t D) {
+    if (check_shapes(dt, B, N, Hq, Hkv, D) != TREE_OK) return 0;
+    if (!use_mfma(dt, Hq, Hkv, D)) return bwd_ws(dt, B, N, Hq, Hkv, D, 0);
+    if (B * N > 0 && !subtree_end) return 0;
+    const int slots = B * N > 0 ? mfma_bwd_plan_slots(subtree_end, (int)B, (int)N, (int)Hq, (int)Hkv) : 0;
+    return bwd_ws(dt, B, N, Hq, Hkv, D, slots);
 }
 
 extern "C" tree_status tree_attn_fwd(tree_dtype dt, const void* q, const void* k, const void* v,
@@ -61,7 +71,8 @@ extern "C" tree_status tree_attn_fwd(tree_dtype dt, const void* q, const void* k
     clear_error();
     tree_status s = check_shapes(dt, B, N, Hq, Hkv, D);
     if (s != TREE_OK) return s;
-    if (!std::isfinite(softmax_scale)) return fail(TREE_ERR_INVALID_ARG, "softmax_scale not finite");
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+        return fail(TREE_ERR_INVALID_ARG, "softmax_scale %g must be finite and positive", (double)softmax_scale);
     if (B == 0 || N == 0) return TREE_OK;
     if (!q || !k || !v || !subtree_end || !out || !lse) return fail(TREE_ERR_INVALID_ARG, "null pointer argument");
     const size_t need = fwd_ws(dt, B, N, Hq, Hkv, D);
@@ -83,17 +94,19 @@ extern "C" tree_status tree_attn_bwd(tree_dtype dt, const void* q, const void* k
     clear_error();
     tree_status s = check_shapes(dt, B, N, Hq, Hkv, D);
     if (s != TREE_OK) return s;
-    if (!std::isfinite(softmax_scale)) return fail(TREE_ERR_INVALID_ARG, "softmax_scale not finite");
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+        return fail(TREE_ERR_INVALID_ARG, "softmax_scale %g must be finite and positive", (double)softmax_scale);
     if (B == 0 || N == 0) return TREE_OK;
     if (!q || !k || !v || !subtree_end || !out || !lse || !dout || !dq || !dk || !dv)
         return fail(TREE_ERR_INVALID_ARG, "null pointer argument");
-    const size_t need = bwd_ws(dt, B, N, Hq, Hkv, D);
+    const size_t need = bwd_ws(dt, B, N, Hq, Hkv, D, 0);  // fixed part; partial-sum slots are what is beyond
     if (ws_bytes < need || !ws) return fail(TREE_ERR_CAPACITY, "workspace %zu < %zu bytes", ws_bytes, need);
     AttnArgs a{dt, q, k, v, subtree_end, (int)B, (int)N, (int)Hq, (int)Hkv, (int)D, softmax_scale,
                const_cast<void*>(out), const_cast<float*>(lse), dout, dq, dk, dv};
     if (use_mfma(dt, Hq, Hkv, D))
         return device_status(
-            mfma_attn_bwd(a, carve_bwd_ws(ws, (int)B, (int)N, (int)Hq, (int)Hkv, (int)D), (hipStream_t)stream),
+            mfma_attn_bwd(a, carve_bwd_ws(ws, ws_bytes, (int)B, (int)N, (int)Hq, (int)Hkv, (int)D),
+                          (hipStream_t)stream),
             "tree_attn_bwd launch");
     return device_status(vec_attn_bwd(a, (float*)ws, (hipStream_t)stream), "tree_attn_bwd launch");
 }

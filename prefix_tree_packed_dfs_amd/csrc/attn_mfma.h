@@ -49,7 +49,8 @@ struct BwdWorkspace {
     int4* tile_plan;     // [B * TT] {first query block, last query block, chunks, first slot or -1}
     int4* units;         // [unit capacity][2] {b*Hkv+g, tile, first visit, end visit}, {slot, 0, 0, 0}
     int4* split_tiles;   // [kSplitSlots/2] {b, tile, first slot, splits}
-    float* partial;      // [kSplitSlots][2][kKvTile][D] fp32 dK, dV partial sums
+    float* partial;      // [slot_cap][2][kKvTile][D] fp32 dK, dV partial sums
+    int slot_cap;        // partial-sum slots the workspace holds (0 .. kSplitSlots)
 };
 
 // Keys per dK/dV workgroup tile, partial-sum slots for split tiles, and the
@@ -69,8 +70,12 @@ int mfma_num_cus();
 size_t mfma_fwd_ws_bytes(int B, int N, int Hkv, int D);
 FwdWorkspace carve_fwd_ws(void* ws, int B, int N, int Hkv, int D);
 hipError_t mfma_attn_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st);
-size_t mfma_bwd_ws_bytes(int B, int N, int Hq, int Hkv, int D);
-BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D);
+// Backward workspace with `slots` partial-sum slots (0 = the fixed part only).
+size_t mfma_bwd_ws_bytes(int B, int N, int Hq, int Hkv, int D, int slots);
+// Partial-sum slots the dK/dV plan of these rows uses at its first budget
+// (capped at kSplitSlots), from subtree_end [B, N] in host memory.
+int mfma_bwd_plan_slots(const int32_t* se, int B, int N, int Hq, int Hkv);
+BwdWorkspace carve_bwd_ws(void* ws, size_t ws_bytes, int B, int N, int Hq, int Hkv, int D);
 hipError_t mfma_attn_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st);
 
 }  // namespace treeattn

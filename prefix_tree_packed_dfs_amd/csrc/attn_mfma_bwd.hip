@@ -30,6 +30,7 @@
 #include <algorithm>
 #include <climits>
 #include <type_traits>
+#include <vector>
 
 #include "attn_mfma.h"
 #include "mfma_common.h"
@@ -53,8 +54,8 @@ __device__ __forceinline__ T ld16(const void* p) {
 // prefix visit almost the whole row while keys near the leaves visit a few
 // blocks, so a tile whose range exceeds C blocks is cut at multiples of C
 // (absolute block positions, C = budget / G; the budget grows by a quarter
-// until the chunks fit the partial-sum slots, so it stays within 25% of the
-// smallest that fits).  Each KV head has its own queue (g mod
+// until the chunks fit the partial-sum slots the workspace holds, so it stays
+// within 25% of the smallest that fits; with no slots no tile is split).  Each KV head has its own queue (g mod
 // NQ, so one XCD keeps one head's data), ordered longest unit first so that
 // the CUs of an XCD run out of work together.  The order of units of equal
 // length is arbitrary; every unit's result is the same whatever the order.
@@ -99,7 +100,7 @@ constexpr int kPlanLds = 64 + kPlanBuckets;
 
 template <int NT>
 __device__ void make_plan(const int32_t* __restrict__ tmax, const int32_t* __restrict__ tiso, int B, int N, int T,
-                          int G, int Hkv, int* __restrict__ ctrl, int4* __restrict__ tile_plan,
+                          int G, int Hkv, int slot_cap, int* __restrict__ ctrl, int4* __restrict__ tile_plan,
                           int4* __restrict__ units, int4* __restrict__ split_tiles, int* lds) {
     static_assert(kPlanBuckets % NT == 0 && NT % 64 == 0 && NT / 64 <= 48, "bucket scan layout");
     int& s_sum = lds[0];
@@ -135,7 +136,7 @@ __device__ void make_plan(const int32_t* __restrict__ tmax, const int32_t* __res
         }
         if (part) atomicAdd(&s_sum, part);
         __syncthreads();
-        const bool fits = (int64_t)s_sum * Hkv <= kSplitSlots;
+        const bool fits = (int64_t)s_sum * Hkv <= slot_cap;
         __syncthreads();
         if (fits) break;
         if (tid == 0) s_budget += max(1, s_budget / 4);
@@ -154,7 +155,7 @@ __device__ void make_plan(const int32_t* __restrict__ tmax, const int32_t* __res
         }
         my_units += nc;
     }
-    // chunk and split counts are at most kSplitSlots: pack both in one scan
+    // chunk and split counts are at most slot_cap <= kSplitSlots: pack both in one scan
     const int packed = block_exclusive_scan<NT>(my_chunks | (my_split << 16), s_scan);
     const int n_units = [&] {
         const int before = block_exclusive_scan<NT>(my_units, s_scan);
@@ -842,7 +843,7 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
 struct PlanArgs {
     const int32_t* tmax;
     const int32_t* tiso;
-    int B, N, T, G, Hkv;
+    int B, N, T, G, Hkv, slot_cap;
     int* ctrl;
     int4* tile_plan;
     int4* units;
@@ -852,9 +853,9 @@ struct PlanArgs {
 // The plan by one 512-thread workgroup of the dQ kernel; out of line, so the
 // dQ items' registers are allocated without it.
 __device__ __attribute__((noinline)) void plan_in_wg(const int32_t* tmax, const int32_t* tiso, int B, int N, int T,
-                                                     int G, int Hkv, int* ctrl, int4* tile_plan, int4* units,
-                                                     int4* split_tiles, int* lds) {
-    make_plan<512>(tmax, tiso, B, N, T, G, Hkv, ctrl, tile_plan, units, split_tiles, lds);
+                                                     int G, int Hkv, int slot_cap, int* ctrl, int4* tile_plan,
+                                                     int4* units, int4* split_tiles, int* lds) {
+    make_plan<512>(tmax, tiso, B, N, T, G, Hkv, slot_cap, ctrl, tile_plan, units, split_tiles, lds);
 }
 
 // One unit of isolated-slot work of the backward: part `unit % kIsoSplit` of
@@ -929,8 +930,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
     // kernel); the others meanwhile take its share of the items
     if (blockIdx.x == gridDim.x - 1) {
         static_assert(kPlanLds * 4 <= 4 * STAGE, "plan scratch fits the stages");
-        plan_in_wg(plan.tmax, plan.tiso, plan.B, plan.N, plan.T, plan.G, plan.Hkv, plan.ctrl, plan.tile_plan,
-                   plan.units, plan.split_tiles, reinterpret_cast<int*>(smem));
+        plan_in_wg(plan.tmax, plan.tiso, plan.B, plan.N, plan.T, plan.G, plan.Hkv, plan.slot_cap, plan.ctrl,
+                   plan.tile_plan, plan.units, plan.split_tiles, reinterpret_cast<int*>(smem));
         __syncthreads();
     }
     const int n_units = qctr[kIsoCount] * kIsoSplit;  // isolated-slot units
@@ -978,8 +979,8 @@ hipError_t launch_dq(const AttnArgs& a, const BwdWorkspace& w, int T, hipStream_
                        w.delta, w.lse2, a.se, w.tile_min, w.tile_max, w.tile_iso, a.B, a.N, a.Hq, a.Hkv, T,
                        n_qtiles, n_chunks, a.scale * kLog2e, a.scale, (__bf16*)a.dq, (__bf16*)a.dk, (__bf16*)a.dv,
                        w.iso_list, w.qctr, NQ, (int)items,
-                       PlanArgs{w.tile_max, w.tile_iso, a.B, a.N, T, a.Hq / a.Hkv, a.Hkv, w.ctrl, w.tile_plan, w.units,
-                                w.split_tiles});
+                       PlanArgs{w.tile_max, w.tile_iso, a.B, a.N, T, a.Hq / a.Hkv, a.Hkv, w.slot_cap, w.ctrl,
+                                w.tile_plan, w.units, w.split_tiles});
     return hipGetLastError();
 }
 
@@ -1011,23 +1012,64 @@ hipError_t launch_bwd(const AttnArgs& a, const BwdWorkspace& w, hipStream_t st) 
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-size_t plan_bytes(int B, int N, int Hkv, int D) {
+// Plan tables (queue control, per-tile plan, unit queues, split-tile table)
+// sized for the largest partial-sum capacity, and the bytes of one slot.
+size_t plan_table_bytes(int B, int N, int Hkv) {
     const size_t TT = (size_t)(N + kKvTile - 1) / kKvTile;
     const size_t ucap = (size_t)kSplitSlots + (size_t)B * TT * Hkv;
     return align256(32 * sizeof(int)) + align256((size_t)B * TT * sizeof(int4)) +
-           align256(ucap * 2 * sizeof(int4)) + align256((size_t)(kSplitSlots / 2) * sizeof(int4)) +
-           align256((size_t)kSplitSlots * 2 * kKvTile * D * sizeof(float));
+           align256(ucap * 2 * sizeof(int4)) + align256((size_t)(kSplitSlots / 2) * sizeof(int4));
 }
+size_t slot_bytes(int D) { return (size_t)2 * kKvTile * D * sizeof(float); }
 
 }  // namespace
 
-size_t mfma_bwd_ws_bytes(int B, int N, int Hq, int Hkv, int D) {
+size_t mfma_bwd_ws_bytes(int B, int N, int Hq, int Hkv, int D, int slots) {
     const size_t T = (size_t)(N + KT - 1) / KT;
     return 2 * align256((size_t)B * Hq * N * sizeof(float)) + 4 * align256((size_t)B * T * sizeof(int32_t)) +
-           align256(kQueueCounters * sizeof(int32_t)) + plan_bytes(B, N, Hkv, D);
+           align256(kQueueCounters * sizeof(int32_t)) + plan_table_bytes(B, N, Hkv) +
+           (size_t)std::min(std::max(slots, 0), kSplitSlots) * slot_bytes(D);
 }
 
-BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D) {
+int mfma_bwd_plan_slots(const int32_t* se, int B, int N, int Hq, int Hkv) {
+    // the device plan's first budget on the device's tile ranges: the tile
+    // ranges kernels (smallest / largest subtree_end per 64-key tile, isolated
+    // tiles) and make_plan's chunk count, recomputed here from the host row
+    const int T = (N + KT - 1) / KT, TT = (N + kKvTile - 1) / kKvTile;
+    const int G = Hq / Hkv, C = std::max(1, kVisitBudget / G);
+    constexpr int SUB = kKvTile / KT, BPT = kKvTile / 32;
+    std::vector<int> tmax(T), tiso(T);
+    int64_t chunks = 0;
+    for (int b = 0; b < B; ++b) {
+        const int32_t* row = se + (int64_t)b * N;
+        int before = -1;  // largest subtree_end of the keys before tile t
+        for (int t = 0; t < T; ++t) {
+            int mx = -1;
+            bool self_only = true;
+            for (int j = t * KT; j < std::min(N, t * KT + KT); ++j) {
+                mx = std::max(mx, row[j]);
+                self_only = self_only && row[j] == j;
+            }
+            tmax[t] = mx;
+            tiso[t] = self_only && before < t * KT;
+            before = std::max(before, mx);
+        }
+        for (int tt = 0; tt < TT; ++tt) {
+            int qmax = -1;
+            bool iso = true;
+            for (int x = SUB * tt; x < std::min(SUB * tt + SUB, T); ++x) {
+                qmax = std::max(qmax, tmax[x]);
+                iso = iso && tiso[x];
+            }
+            if (iso) continue;
+            const int first = BPT * tt, last = std::max(qmax / 32, BPT * tt);
+            if (last - first + 1 > C) chunks += last / C - first / C + 1;
+        }
+    }
+    return (int)std::min<int64_t>(kSplitSlots, chunks * Hkv);
+}
+
+BwdWorkspace carve_bwd_ws(void* ws, size_t ws_bytes, int B, int N, int Hq, int Hkv, int D) {
     const size_t T = (size_t)(N + KT - 1) / KT;
     char* p = static_cast<char*>(ws);
     BwdWorkspace w;
@@ -1056,6 +1098,9 @@ BwdWorkspace carve_bwd_ws(void* ws, int B, int N, int Hq, int Hkv, int D) {
     w.split_tiles = reinterpret_cast<int4*>(p);
     p += align256((size_t)(kSplitSlots / 2) * sizeof(int4));
     w.partial = reinterpret_cast<float*>(p);
+    // the partial-sum slots are what the workspace holds beyond the fixed part
+    const size_t fixed = mfma_bwd_ws_bytes(B, N, Hq, Hkv, D, 0);
+    w.slot_cap = ws_bytes > fixed ? (int)std::min<size_t>(kSplitSlots, (ws_bytes - fixed) / slot_bytes(D)) : 0;
     return w;
 }
 

@@ -32,6 +32,7 @@
 // order the accumulator holds them.  Online softmax in fp32 with exp2 and a
 // log2(e)-prescaled scale; P is rounded to bf16 for the PV product.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 
 #include "attn_mfma.h"
@@ -575,15 +576,17 @@ hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, in
 }
 
 int mfma_num_cus() {
-    static int cached[64] = {0};
+    // A per-device value written once: racing first calls store the same
+    // number, and the atomics make the sharing between threads well defined.
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 hipError_t mfma_attn_fwd(const AttnArgs& a, const FwdWorkspace& w, hipStream_t st) {

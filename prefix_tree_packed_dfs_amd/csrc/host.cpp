@@ -31,7 +31,7 @@ void clear_error() { g_last_error[0] = '\0'; }
 
 using treeattn::fail;
 
-extern "C" int tree_abi_version(void) { return 4; }
+extern "C" int tree_abi_version(void) { return 5; }
 
 extern "C" const char* tree_status_string(int s) {
     switch (s) {

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert declared == set(lib.EXPORTED)
     for name in declared:
         assert hasattr(lib.lib, name), name
-    assert lib.lib.tree_abi_version() == 4
+    assert lib.lib.tree_abi_version() == 5
 
 
 def _random_sequences(rng, n, max_len, vocab):
@@ -185,3 +185,78 @@ def test_sequence_packing_forest_is_plain_varlen_causal(seed):
     assert np.array_equal(lay.subtree_end[total:], np.arange(total, R))
     rl = dfs_layout(parent, seq_last, R)
     assert np.array_equal(lay.subtree_end, rl.subtree_end) and np.array_equal(lay.pos_ids, rl.pos_ids)
+
+
+def test_softmax_scale_must_be_finite_and_positive():
+    """The matrix-core forward masks raw scores and scales afterwards, so a zero or negative scale would
+    give NaN or wrong maxima: both device entry points refuse it before any launch."""
+    L = lib.lib
+    for scale in (0.0, -0.125, float("nan"), float("inf")):
+        assert L.tree_attn_fwd(1, None, None, None, None, 1, 8, 4, 2, 64, scale, None, None, None, 0, None) == 1
+        assert "softmax_scale" in lib.lib.tree_last_error().decode()
+        assert L.tree_attn_bwd(1, *([None] * 7), 1, 8, 4, 2, 64, scale, None, None, None, None, 0, None) == 1
+    # a positive scale passes this check and fails later on the null pointers
+    assert L.tree_attn_fwd(1, None, None, None, None, 1, 8, 4, 2, 64, 0.125, None, None, None, 0, None) == 1
+    assert "null" in lib.lib.tree_last_error().decode()
+
+
+def test_output_buffers_are_checked_before_any_launch():
+    """Caller-supplied out / lse / dq / dk / dv of the wrong shape or dtype raise ValueError in the
+    binding before a pointer reaches the library (CPU tensors: nothing is launched)."""
+    import torch
+    B, N, Hq, Hkv, D = 1, 16, 4, 2, 64
+    q = torch.zeros(B, N, Hq, D, dtype=torch.bfloat16)
+    k = torch.zeros(B, N, Hkv, D, dtype=torch.bfloat16)
+    v = torch.zeros_like(k)
+    se = torch.arange(N, dtype=torch.int32).view(B, N)
+    lse = torch.zeros(B, Hq, N, dtype=torch.float32)
+    bad = {
+        "out": [torch.zeros(B, N, Hq, D - 1, dtype=torch.bfloat16), torch.zeros(B, N, Hq, D, dtype=torch.float32)],
+        "lse": [torch.zeros(B, Hq, N - 1, dtype=torch.float32), torch.zeros(B, Hq, N, dtype=torch.bfloat16)],
+    }
+    for name, cases in bad.items():
+        for t in cases:
+            with pytest.raises(ValueError, match=name):
+                lib.tree_attn_fwd(q, k, v, se, **{name: t})
+    for name, good in (("dq", q), ("dk", k), ("dv", v)):
+        for t in (torch.zeros(*good.shape[:-1], D // 2, dtype=good.dtype), good.to(torch.float32),
+                  torch.zeros(B, N + 1, *good.shape[2:], dtype=good.dtype)):
+            with pytest.raises(ValueError, match=name):
+                lib.tree_attn_bwd(q, k, v, se, q, lse, q, **{name: t})
+
+
+def test_backward_workspace_sized_to_the_rows_plan():
+    """tree_attn_bwd_workspace_bytes_for: the fixed part for rows whose key tiles are all short (nothing
+    cut into chunks), the fixed part plus some partial-sum slots for a shared prompt, and the largest
+    workspace once the rows would need more slots than it holds."""
+    L = lib.lib
+    BF16, F32 = lib.TREE_BF16, lib.TREE_F32
+    full = lib.tree_attn_workspace_bytes(BF16, 1, 32768, 16, 8, 128, True)
+    pad = np.arange(32768, dtype=np.int32)          # every slot isolated: no units, no cut tiles
+    fixed = lib.tree_attn_bwd_workspace_bytes_for(BF16, pad, 16, 8, 128)
+    slot = 2 * 256 * 128 * 4
+    assert 0 < fixed < full and (full - fixed) == 1536 * slot
+    sizes = {}
+    for c in (2, 3, 4, 5):
+        w = standard(c)
+        parent, seq_last = lib.tree_build_trie(w.sequences, min_shared=64)
+        R = w.row_length(len(parent))
+        se = lib.tree_pack_layout(parent, seq_last, R).subtree_end
+        got = lib.tree_attn_bwd_workspace_bytes_for(BF16, se, w.Hq, w.Hkv, w.D)
+        base = lib.tree_attn_bwd_workspace_bytes_for(BF16, np.arange(R, dtype=np.int32), w.Hq, w.Hkv, w.D)
+        top = lib.tree_attn_workspace_bytes(BF16, 1, R, w.Hq, w.Hkv, w.D, True)
+        assert base <= got <= top and (got - base) % slot == 0
+        sizes[w.name] = (got - base) // slot
+        # two rows need what each needs, summed (capped)
+        two = lib.tree_attn_bwd_workspace_bytes_for(BF16, np.stack([se, se]), w.Hq, w.Hkv, w.D)
+        base2 = lib.tree_attn_bwd_workspace_bytes_for(BF16, np.stack([np.arange(R, dtype=np.int32)] * 2),
+                                                     w.Hq, w.Hkv, w.D)
+        assert (two - base2) // slot == min(1536, 2 * sizes[w.name])
+    assert sizes["independent"] == 0                # 512-token sequences: no key tile sees far enough
+    assert 0 < sizes["grpo_group"] < 1536            # the prompt's tiles are cut, a share of the slots
+    assert sizes["long_history"] == 1536             # the 20,000-token history wants more than the cap
+    # the vector path needs delta only; bad arguments give 0
+    assert lib.tree_attn_bwd_workspace_bytes_for(F32, pad[:100], 2, 2, 64) == \
+        lib.tree_attn_workspace_bytes(F32, 1, 100, 2, 2, 64, True)
+    assert L.tree_attn_bwd_workspace_bytes_for(BF16, None, 1, 64, 4, 2, 64) == 0
+    assert L.tree_attn_bwd_workspace_bytes_for(BF16, None, 1, 64, 4, 2, 96) == 0

@@ -164,6 +164,32 @@ def test_sampled_mode_matches_full():
     assert np.allclose(part.dv[ks], full.dv[ks], atol=1e-12)
 
 
+@pytest.mark.parametrize("Hq,Hkv,heads", [(4, 2, [1]), (6, 2, [0]), (8, 4, [0, 3])])
+def test_kv_head_subset_matches_full(Hq, Hkv, heads):
+    """Restricting the work to some KV heads (their whole query-head groups) leaves every output of those
+    heads as in the full run, alone and together with sampled slots; the other heads are not computed."""
+    seqs, fids, dkeys, tables = _random_case(17, n_seqs=6, max_len=20, Hq=Hq, Hkv=Hkv)
+    full = tree_attention(seqs, fids, dkeys, tables, theta=10.0, min_shared=1)
+    n = full.layout.n_nodes
+    G = Hq // Hkv
+    qh = [g * G + i for g in heads for i in range(G)]
+    other_q = [h for h in range(Hq) if h not in qh]
+    other_kv = [g for g in range(Hkv) if g not in heads]
+    part = tree_attention(seqs, fids, dkeys, tables, theta=10.0, min_shared=1, kv_heads=heads)
+    for a, b in ((part.out[:n, qh], full.out[:n, qh]), (part.lse[qh][:, :n], full.lse[qh][:, :n]),
+                 (part.dq[:n, qh], full.dq[:n, qh]), (part.dk[:n, heads], full.dk[:n, heads]),
+                 (part.dv[:n, heads], full.dv[:n, heads])):
+        assert np.allclose(a, b, atol=1e-12, rtol=0)
+    assert np.all(np.isnan(part.out[:, other_q])) and np.all(np.isnan(part.dq[:, other_q]))
+    if other_kv:
+        assert np.all(np.isnan(part.dk[:, other_kv])) and np.all(np.isnan(part.dv[:, other_kv]))
+    rng = np.random.default_rng(1)
+    ks = rng.choice(n, size=min(5, n), replace=False)
+    both = tree_attention(seqs, fids, dkeys, tables, theta=10.0, min_shared=1, kv_heads=heads, k_slots=ks)
+    assert np.allclose(both.dk[ks][:, heads], full.dk[ks][:, heads], atol=1e-12, rtol=0)
+    assert np.allclose(both.dv[ks][:, heads], full.dv[ks][:, heads], atol=1e-12, rtol=0)
+
+
 def test_gradient_sums_hold():
     """sum_j dV[j] = sum_i dout[i] per KV head; sum_j dK[j] = 0 (softmax rows sum to one)."""
     seqs, fids, dkeys, tables = _random_case(13)
