@@ -304,11 +304,14 @@ def _shapes(q, k, v, subtree_end):
 
 
 def _workspace(dt, B, N, Hq, Hkv, D, bwd, ws, device):
+    """The caller's workspace, or the largest one these sizes can use.  A backward workspace smaller
+    than that is the caller's choice (the library takes fewer partial-sum slots, down to its fixed
+    part, and reports TREE_ERR_CAPACITY below it)."""
     torch = _torch()
     need = tree_attn_workspace_bytes(dt, B, N, Hq, Hkv, D, bwd)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-    if ws.numel() * ws.element_size() < need:
+    if not bwd and ws.numel() * ws.element_size() < need:
         raise ValueError(f"workspace needs {need} bytes")
     return ws
 

@@ -9,7 +9,7 @@ import pytest
 from synth import (agentic_trie, feature_tables, from_sequences, grpo_group, independent, long_history,
                    standard, tiny_tree)
 
-from .pipeline import assert_within, compare, log, run_library, run_oracle, timed
+from .pipeline import assert_within, cmp, compare, log, run_library, run_oracle, timed
 
 pytestmark = pytest.mark.gpu
 
@@ -34,11 +34,11 @@ def _random_workload(seed, dtype, Hq, Hkv, D, n_seqs=6, max_len=300, vocab=2, fo
     return from_sequences(seqs, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, seed_base=10_000 + seed)
 
 
-def _run_full(w, rope=True, label=""):
+def _run_full(w, rope=True, label="", ws_mode=None):
     log(f"case {label or w.name}: dtype={w.dtype} Hq={w.Hq} Hkv={w.Hkv} D={w.D} seqs={len(w.sequences)} "
-        f"raw={w.raw_tokens} seed={w.seed_base}")
+        f"raw={w.raw_tokens} seed={w.seed_base} bwd workspace={ws_mode or 'largest'}")
     tables = feature_tables(w)
-    lres = timed("library", run_library, w, tables, rope=rope)
+    lres = timed("library", run_library, w, tables, rope=rope, ws_mode=ws_mode)
     ores = timed("oracle", run_oracle, w, tables, rope=rope, R=lres.R)
     rows = compare(w, lres, ores)
     assert_within(w, rows)
@@ -223,6 +223,49 @@ def _run_sampled(w, label, n_q=256, tail=256):
     assert np.allclose(lres.dv[:n].sum(axis=0), do_sum, atol=0.05 * np.abs(do_sum).max() + 0.5)
     assert np.abs(lres.dk[:n].sum(axis=0)).max() < 0.05 * np.sqrt(n * G)
     assert np.all(np.isfinite(lres.out[:n])) and np.all(np.isfinite(lres.dq[:n]))
+    return lres, tables
+
+
+def _check_shared_keys(w, lres, tables, label, per_group=16, kv_head=0):
+    """dk, dv at keys many queries see, against the oracle restricted to one KV head (its whole
+    query-head group, so each output is exact): random keys of the segment every sequence shares
+    (the root), the deepest 512 of them (the end of a shared history), and keys of segments shared by
+    some sequences but not all (inner segments).  These keys carry most of the dK/dV work, and on long
+    rows their key tiles are the ones the dK/dV plan cuts into chunks whose partial sums are added by
+    the reduce pass."""
+    from oracle.layout import dfs_layout
+    from oracle.trie import build_trie
+
+    n_seqs = len(w.sequences)
+    counts = np.zeros(lres.R, np.int64)
+    for s in range(n_seqs):
+        counts[lres.layout.sequence_slots(s)] += 1
+    real = np.arange(lres.n)
+    root = real[counts[:lres.n] == n_seqs]
+    inner = real[(counts[:lres.n] >= 2) & (counts[:lres.n] < n_seqs)]
+    rng = np.random.default_rng(w.seed_base + 7)
+    picks = []
+    if len(root):
+        picks += list(rng.choice(root, min(per_group, len(root)), replace=False))
+        deep = root[np.argsort(lres.layout.pos_ids[root], kind="stable")[-512:]]
+        picks += list(rng.choice(deep, min(per_group, len(deep)), replace=False))
+    if len(inner):
+        picks += list(rng.choice(inner, min(per_group, len(inner)), replace=False))
+    picks = np.unique(np.asarray(picks, np.int64))
+    assert len(picks), "no shared keys"
+    # library slot -> oracle slot through the sequences' paths
+    trie = build_trie(w.sequences)
+    olay = dfs_layout(trie.parent, trie.seq_last, lres.R)
+    m = np.full(lres.R, -1, np.int64)
+    for s in range(n_seqs):
+        m[lres.layout.sequence_slots(s)] = olay.token_index[s]
+    depths = lres.layout.pos_ids[picks]
+    log(f"  shared keys {label}: {len(picks)} keys (root {len(root)}, inner {len(inner)} slots), depths "
+        f"{int(depths.min())}..{int(depths.max())}, KV head {kv_head}")
+    ores = timed("oracle, one KV head", run_oracle, w, tables, R=lres.R, k_slots=m[picks], kv_heads=[kv_head])
+    rows = [cmp("dk@shared", lres.dk[picks, kv_head], ores.dk[m[picks], kv_head], w.dtype),
+            cmp("dv@shared", lres.dv[picks, kv_head], ores.dv[m[picks], kv_head], w.dtype)]
+    assert_within(w, rows)
 
 
 def _dout_sum(w, tables, lres):
@@ -242,11 +285,122 @@ def test_long_chain_beyond_one_tile_list_sampled():
 
 
 def test_full_c3_agentic_sampled():
-    _run_sampled(standard(3), "full_agentic_trie")
+    w = standard(3)
+    lres, tables = _run_sampled(w, "full_agentic_trie")
+    _check_shared_keys(w, lres, tables, "full_agentic_trie")
 
 
 def test_full_c5_long_history_sampled():
-    _run_sampled(standard(5), "full_long_history")
+    w = standard(5)
+    lres, tables = _run_sampled(w, "full_long_history")
+    _check_shared_keys(w, lres, tables, "full_long_history")
+
+
+def _split_prompt(tail=300, prompt=4000, n=4):
+    rng = np.random.default_rng(31)
+    base = np.arange(prompt, dtype=np.int32)
+    seqs = [np.concatenate([base, 10_000 + 1000 * i + rng.permutation(tail).astype(np.int32)]) for i in range(n)]
+    return from_sequences(seqs, Hq=32, Hkv=8, D=128, dtype="bf16", seed_base=16_000, name="split_prompt")
+
+
+@pytest.mark.parametrize("ws_mode", [None, "fixed"])
+def test_split_prompt_tiles_gqa4_every_element(ws_mode):
+    """A 4,000-token prompt and four 300-token tails at 32 query / 8 KV heads, every element against
+    the oracle.  Four query heads per KV head make the dK/dV plan's chunk 80 query blocks, so the
+    prompt's key tiles (whose keys every tail sees) are cut into chunks that write partial sums and the
+    reduce pass adds them; with the fixed-only workspace nothing is cut and each tile is one unit."""
+    import prefix_tree_packed_dfs_amd as lib
+    w = _split_prompt()
+    parent, seq_last = lib.tree_build_trie(w.sequences, min_shared=64)
+    R = w.row_length(len(parent))
+    se = lib.tree_pack_layout(parent, seq_last, R).subtree_end
+    slots = (lib.tree_attn_bwd_workspace_bytes_for(lib.TREE_BF16, se, w.Hq, w.Hkv, w.D)
+             - lib.tree_attn_bwd_workspace_bytes_for(lib.TREE_BF16, np.arange(R, dtype=np.int32), w.Hq, w.Hkv, w.D)
+             ) // (2 * 256 * 128 * 4)
+    log(f"  split_prompt: {len(parent)} slots, the plan takes {slots} partial-sum slots")
+    assert slots > 0
+    _run_full(w, label=f"split_prompt_gqa4[{ws_mode or 'largest'}]", ws_mode=ws_mode)
+
+
+def test_backward_workspace_exact_size_gives_the_same_results():
+    """grpo_group at full size: the backward with the exact workspace of its plan is bitwise the
+    backward with the largest workspace (the same plan); with the fixed part only, nothing is cut into
+    chunks and the results differ by the order of summation only."""
+    import torch
+
+    import prefix_tree_packed_dfs_amd as lib
+    from .pipeline import bwd_workspace
+    w = standard(2)
+    log(f"case workspace sizes: {w.name} Hq={w.Hq} Hkv={w.Hkv} D={w.D}")
+    parent, seq_last = lib.tree_build_trie(w.sequences, min_shared=64)
+    R = w.row_length(len(parent))
+    lay = lib.tree_pack_layout(parent, seq_last, R)
+    se = torch.from_numpy(lay.subtree_end.astype(np.int32)).view(1, R).cuda()
+    g = torch.Generator().manual_seed(9)
+    mk = lambda H: torch.randn(1, R, H, w.D, generator=g).to(torch.bfloat16).cuda()  # noqa: E731
+    q, k, v, do = mk(w.Hq), mk(w.Hkv), mk(w.Hkv), mk(w.Hq)
+    out, lse = lib.tree_attn_fwd(q, k, v, se)
+    res = {}
+    for mode in (None, "exact", "fixed"):
+        ws = bwd_workspace(w, lay, R, mode)
+        res[mode] = lib.tree_attn_bwd(q, k, v, se, out, lse, do, ws=ws)
+        torch.cuda.synchronize()
+        log(f"    {mode or 'largest'}: {ws.numel() if ws is not None else 'default'} bytes")
+    for a, b in zip(res[None], res["exact"]):
+        assert torch.equal(a, b)
+    for a, b in zip(res[None], res["fixed"]):
+        a, b = a.float(), b.float()
+        e = float(((a - b).abs() - 2.0 ** -7 * b.abs()).max())
+        log(f"    fixed-only vs largest: max|d| {float((a - b).abs().max()):.3e}, beyond one ulp {e:.3e}")
+        assert e <= 1e-2
+
+
+def test_outputs_stay_inside_their_buffers():
+    """Guard bands of sentinel values before and after out, lse, dq, dk, dv and both workspaces
+    (grpo_group at full size, each buffer a view into a larger one): after the forward and the
+    backward every sentinel is still there, and every output element was written."""
+    import torch
+
+    import prefix_tree_packed_dfs_amd as lib
+    w = standard(2)
+    log(f"case guard bands: {w.name}")
+    parent, seq_last = lib.tree_build_trie(w.sequences, min_shared=64)
+    R = w.row_length(len(parent))
+    lay = lib.tree_pack_layout(parent, seq_last, R)
+    se = torch.from_numpy(lay.subtree_end.astype(np.int32)).view(1, R).cuda()
+    g = torch.Generator().manual_seed(10)
+    mk = lambda H: torch.randn(1, R, H, w.D, generator=g).to(torch.bfloat16).cuda()  # noqa: E731
+    q, k, v, do = mk(w.Hq), mk(w.Hkv), mk(w.Hkv), mk(w.Hq)
+    GUARD = 4096
+    bands = []
+
+    def guarded(shape, dtype, sentinel):
+        numel = int(np.prod(shape))
+        full = torch.full((GUARD + numel + GUARD,), sentinel, dtype=dtype, device="cuda")
+        bands.append((full, numel, sentinel))
+        return full[GUARD:GUARD + numel].view(shape)
+
+    NAN16 = float("nan")
+    out = guarded((1, R, w.Hq, w.D), torch.bfloat16, NAN16)
+    lse = guarded((1, w.Hq, R), torch.float32, float("nan"))
+    dq = guarded((1, R, w.Hq, w.D), torch.bfloat16, NAN16)
+    dk = guarded((1, R, w.Hkv, w.D), torch.bfloat16, NAN16)
+    dv = guarded((1, R, w.Hkv, w.D), torch.bfloat16, NAN16)
+    wsf = guarded((lib.tree_attn_workspace_bytes(lib.TREE_BF16, 1, R, w.Hq, w.Hkv, w.D, False),), torch.uint8, 0xA5)
+    wsb = guarded((lib.tree_attn_bwd_workspace_bytes_for(lib.TREE_BF16, lay.subtree_end, w.Hq, w.Hkv, w.D),),
+                  torch.uint8, 0x5A)
+    lib.tree_attn_fwd(q, k, v, se, out=out, lse=lse, ws=wsf)
+    lib.tree_attn_bwd(q, k, v, se, out, lse, do, dq=dq, dk=dk, dv=dv, ws=wsb)
+    torch.cuda.synchronize()
+    for full, numel, sentinel in bands:
+        for part in (full[:GUARD], full[GUARD + numel:]):
+            if isinstance(sentinel, float) and np.isnan(sentinel):
+                assert bool(torch.isnan(part.float()).all()), "a guard band was written"
+            else:
+                assert bool((part == sentinel).all()), "a guard band was written"
+    for t in (out, lse, dq, dk, dv):
+        assert not bool(torch.isnan(t.float()).any()), "an output element was not written"
+    log(f"    {len(bands)} buffers: guard bands intact, every output element written")
 
 
 # ---------------------------------------------------------------------------

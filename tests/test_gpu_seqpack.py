@@ -23,7 +23,7 @@ import pytest
 from synth import (agentic_trie, feature_tables, from_sequences, grpo_group, long_history, sequence_packing_forest,
                    shared_history)
 
-from .pipeline import log
+from .pipeline import assert_within, cmp, log, timed
 
 pytestmark = pytest.mark.gpu
 
@@ -199,3 +199,58 @@ def test_agentic_trie_full():
 
 def test_long_history_full():
     _compare_layouts(long_history(), "seqpack long_history (20000 + 8 x 2000)")
+
+
+def _chains_vs_oracle(w, label):
+    """The sequence-packed row (one chain per sequence, plain varlen causal attention) through the C ABI
+    against the oracle run on each sequence alone, token by token: out, lse, and with the upstream
+    gradient on every token, dq, dk and dv of every copy.  The oracle shares no code with the layout or
+    the kernels, so this checks the baseline side of the tree-vs-sequence-packing comparison directly."""
+    import torch
+
+    from oracle.attention import tree_attention
+    log(f"case {label}: dtype={w.dtype} Hq={w.Hq} Hkv={w.Hkv} D={w.D} seqs={len(w.sequences)} raw={w.raw_tokens} "
+        f"seed={w.seed_base}")
+    dev = torch.device("cuda", 0)
+    tables_np = feature_tables(w)
+    tables = {k: torch.from_numpy(v).to(dev) for k, v in tables_np.items()}
+    chains = _Row(w, tables, *sequence_packing_forest(w.sequences))
+    assert chains.n == w.raw_tokens
+    chains.forward()
+    dq, dk, dv = chains.backward(chains.do)
+    torch.cuda.synchronize()
+
+    def host(t):
+        return t[0].double().cpu().numpy()
+
+    lib_t = {"out": host(chains.out), "lse": chains.lse[0].double().cpu().numpy(), "dq": host(dq), "dk": host(dk),
+             "dv": host(dv)}
+    got = {k: [] for k in lib_t}
+    want = {k: [] for k in lib_t}
+
+    def oracle_all():
+        for s in range(len(w.sequences)):
+            o = tree_attention([w.sequences[s]], [w.fid[s]], [w.dkey[s]], tables_np, theta=w.theta, storage=w.dtype)
+            cs = chains.lay.sequence_slots(s).astype(np.int64)
+            os_ = o.layout.token_index[0]
+            for k in ("out", "dq", "dk", "dv"):
+                got[k].append(lib_t[k][cs])
+                want[k].append(getattr(o, k)[os_])
+            got["lse"].append(lib_t["lse"][:, cs])
+            want["lse"].append(o.lse[:, os_])
+
+    timed("oracle, per sequence", oracle_all)
+    rows = []
+    for k in ("out", "lse", "dq", "dk", "dv"):
+        ax = 1 if k == "lse" else 0
+        rows.append(cmp(k, np.concatenate(got[k], axis=ax), np.concatenate(want[k], axis=ax),
+                        w.dtype if k != "lse" else None))
+    assert_within(w, rows)
+
+
+def test_sequence_packing_vs_oracle_ragged():
+    _chains_vs_oracle(shared_history(700, n=5, unique=333), "seqpack vs oracle: shared history 700 + 5 x 333")
+
+
+def test_sequence_packing_vs_oracle_grpo_group_full():
+    _chains_vs_oracle(grpo_group(), "seqpack vs oracle: grpo_group (16 x (2048 + 1024), 49,152-slot row)")
