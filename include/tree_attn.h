@@ -13,6 +13,7 @@
  *   tree_rope            rotary embedding at depth, in place (device)
  *   tree_rope_qk         the same on q and k in one launch (device)
  *   tree_attn_fwd        masked attention forward (device)
+ *   tree_attn_fwd_noalloc  the same without a workspace, for callers that cannot allocate (device)
  *   tree_attn_bwd        its exact gradient (device)
  *   tree_gdn_plan        DFS row -> chains, 64-token chunks, depth buckets (host)
  *   tree_gdn_fwd         gated-delta-rule mixing over the row (device)
@@ -295,6 +296,27 @@ tree_status tree_attn_fwd(tree_dtype dt, const void* q, const void* k, const voi
                           const int32_t* subtree_end, int64_t B, int64_t N, int64_t Hq,
                           int64_t Hkv, int64_t D, float softmax_scale, void* out, float* lse,
                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tree_attn_fwd_noalloc - tree_attn_fwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, kernels
+ * and results as tree_attn_fwd; its per-call tables live in a fixed
+ * 1,114,112-byte array of the library's device code (one per GPU, held until
+ * the process ends), so the call itself allocates nothing.
+ *
+ * Limit: B x ceil(N / 64) <= 65,536 (e.g. one row of 4M slots, or 128 rows
+ * of 32K); beyond it TREE_ERR_CAPACITY, before any device call.  The array's
+ * device address is looked up on the first call on each device
+ * (hipGetSymbolAddress; TREE_ERR_DEVICE if that fails).  Every call on one
+ * GPU shares that GPU's array: calls that may run at the same time on one
+ * GPU (other streams, other threads) race and must be serialised by the
+ * caller; a call re-initialises the tables it reads, so nothing carries over
+ * from the previous call.
+ */
+tree_status tree_attn_fwd_noalloc(tree_dtype dt, const void* q, const void* k, const void* v,
+                                  const int32_t* subtree_end, int64_t B, int64_t N, int64_t Hq, int64_t Hkv,
+                                  int64_t D, float softmax_scale, void* out, float* lse, void* stream);
 
 /*
  * tree_attn_bwd - exact gradient of tree_attn_fwd (device).

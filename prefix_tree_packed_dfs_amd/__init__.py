@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     lib,
     tree_attn_bwd,
     tree_attn_fwd,
+    tree_attn_fwd_noalloc,
     tree_attn_workspace_bytes,
     tree_attn_bwd_workspace_bytes_for,
     tree_build_trie,

@@ -75,6 +75,9 @@ lib.tree_attn_bwd_workspace_bytes_for.argtypes = [C.c_int, _i32p, C.c_int64, C.c
 lib.tree_attn_fwd.restype = C.c_int
 lib.tree_attn_fwd.argtypes = [C.c_int, _vp, _vp, _vp, _vp, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
                               C.c_int64, C.c_float, _vp, _vp, _vp, C.c_size_t, _vp]
+lib.tree_attn_fwd_noalloc.restype = C.c_int
+lib.tree_attn_fwd_noalloc.argtypes = [C.c_int, _vp, _vp, _vp, _vp, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
+                                      C.c_int64, C.c_float, _vp, _vp, _vp]
 lib.tree_attn_bwd.restype = C.c_int
 lib.tree_attn_bwd.argtypes = [C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int64, C.c_int64, C.c_int64,
                               C.c_int64, C.c_int64, C.c_float, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
@@ -95,7 +98,7 @@ lib.tree_mfma_peak.argtypes = [C.c_int64, C.c_int64, _vp, C.POINTER(C.c_double),
 EXPORTED = ("tree_abi_version", "tree_status_string", "tree_last_error", "tree_build_trie",
             "tree_place_leaves", "tree_pack_layout", "tree_validate_subtree_end", "tree_rope", "tree_rope_qk",
             "tree_attn_workspace_bytes", "tree_attn_bwd_workspace_bytes_for",
-            "tree_attn_fwd", "tree_attn_bwd", "tree_gdn_plan", "tree_gdn_workspace_bytes", "tree_gdn_fwd",
+            "tree_attn_fwd", "tree_attn_fwd_noalloc", "tree_attn_bwd", "tree_gdn_plan", "tree_gdn_workspace_bytes", "tree_gdn_fwd",
             "tree_mfma_peak")
 
 
@@ -332,6 +335,23 @@ def tree_attn_fwd(q, k, v, subtree_end, softmax_scale=None, out=None, lse=None, 
     _check(lib.tree_attn_fwd(dt, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(subtree_end, "subtree_end"),
                              B, N, Hq, Hkv, D, scale, _dev(out, "out"), _dev(lse, "lse"), ws.data_ptr(),
                              ws.numel() * ws.element_size(), _stream()))
+    return out, lse
+
+
+def tree_attn_fwd_noalloc(q, k, v, subtree_end, softmax_scale=None, out=None, lse=None):
+    """tree_attn_fwd with the library's fixed per-GPU table array instead of a workspace; returns (out, lse)."""
+    torch = _torch()
+    B, N, Hq, Hkv, D = _shapes(q, k, v, subtree_end)
+    dt = _dtype_code(q)
+    scale = D ** -0.5 if softmax_scale is None else float(softmax_scale)
+    out = _out(out, "out", q.shape, q.dtype, q)
+    lse = _out(lse, "lse", (B, Hq, N), torch.float32, q)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check(lib.tree_attn_fwd_noalloc(dt, _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(subtree_end, "subtree_end"),
+                                     B, N, Hq, Hkv, D, scale, _dev(out, "out"), _dev(lse, "lse"), _stream()))
     return out, lse
 
 

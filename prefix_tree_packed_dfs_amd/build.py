@@ -25,6 +25,7 @@ SOURCES = [
     "attn_vec.hip",
     "attn_mfma_fwd.hip",
     "attn_mfma_bwd.hip",
+    "attn_noalloc.hip",
     "gdn_api.cpp",
     "gdn.hip",
     "mfma_peak.hip",

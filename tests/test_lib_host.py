@@ -260,3 +260,17 @@ def test_backward_workspace_sized_to_the_rows_plan():
         lib.tree_attn_workspace_bytes(F32, 1, 100, 2, 2, 64, True)
     assert L.tree_attn_bwd_workspace_bytes_for(BF16, None, 1, 64, 4, 2, 64) == 0
     assert L.tree_attn_bwd_workspace_bytes_for(BF16, None, 1, 64, 4, 2, 96) == 0
+
+
+def test_noalloc_forward_refuses_sizes_beyond_its_array_before_any_device_call():
+    """tree_attn_fwd_noalloc holds tables for B x ceil(N / 64) <= 65,536 tiles; beyond that it returns
+    TREE_ERR_CAPACITY before touching the device (no GPU here), and bad arguments get tree_attn_fwd's
+    own errors."""
+    L = lib.lib
+    assert L.tree_attn_fwd_noalloc(1, None, None, None, None, 1, 65536 * 64 + 1, 16, 8, 128, 0.1, None, None,
+                                   None) == 3
+    assert "65536" in L.tree_last_error().decode()
+    assert L.tree_attn_fwd_noalloc(1, None, None, None, None, 129, 32768, 16, 8, 128, 0.1, None, None, None) == 3
+    assert L.tree_attn_fwd_noalloc(1, None, None, None, None, 1, 64, 4, 2, 96, 0.1, None, None, None) == 4
+    assert L.tree_attn_fwd_noalloc(7, None, None, None, None, 1, 64, 4, 2, 64, 0.1, None, None, None) == 1
+    assert L.tree_attn_fwd_noalloc(0, None, None, None, None, 1, 64, 4, 2, 64, 0.0, None, None, None) == 1
