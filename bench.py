@@ -124,8 +124,10 @@ def bench_planner(args):
     """Host row planner on multi-task batches of 12 .. 768 groups, rows of 131,072 tokens.
 
     Times tree_build_trie (trainable mode) and tree_place_leaves (global best-fit decreasing, and
-    in order), as [ART "Does it actually help?"] tables the tree walk against the bin-packing pass;
-    the oracle runs beside it on the smallest batch.  Prints one JSON line."""
+    in order), as [ART "Does it actually help?"] tables the tree walk against the bin-packing pass,
+    and tree_plan_rows (rows grown in order under a 131,072-token budget, fork threshold 1024,
+    [TRL "How tree packing works"]) with its row fill and fork fraction; the oracle runs beside
+    it on the smallest batch.  Prints one JSON line."""
     import numpy as np
 
     import prefix_tree_packed_dfs_amd as lib
@@ -158,10 +160,17 @@ def bench_planner(args):
         t2 = time.perf_counter()
         _, tok_i = lib.tree_place_leaves(parent, seq_last, grp, row, "in_order")
         t3 = time.perf_counter()
+        # TRL's planner on the same samples: rows grown in order under a forwarded-token budget
+        t4 = time.perf_counter()
+        row_of, row_tok, forked = lib.tree_plan_rows(seqs, row, 1024)
+        t5 = time.perf_counter()
         out.append({"groups": n_groups, "completions": len(seqs), "raw_tokens": int(sum(len(x) for x in seqs)),
                     "trie_nodes": int(len(parent)), "trie_ms": round((t1 - t0) * 1e3, 2),
                     "place_global_ms": round((t2 - t1) * 1e3, 2), "rows_global": int(len(tok_g)),
-                    "place_in_order_ms": round((t3 - t2) * 1e3, 2), "rows_in_order": int(len(tok_i))})
+                    "place_in_order_ms": round((t3 - t2) * 1e3, 2), "rows_in_order": int(len(tok_i)),
+                    "plan_rows_ms": round((t5 - t4) * 1e3, 2), "rows_plan": int(len(row_tok)),
+                    "plan_row_fill": round(float(row_tok.sum()) / (len(row_tok) * row), 4),
+                    "plan_fork_frac": round(float(forked.mean()), 4)})
     oracle = None
     if not args.no_cpu_baseline:
         from oracle.pack import place_leaves, segments

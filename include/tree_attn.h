@@ -9,6 +9,7 @@
  *
  *   tree_build_trie      token sequences -> token-level parent array (host)
  *   tree_place_leaves    sequences of a trie -> fixed-length rows (host)
+ *   tree_plan_rows       samples -> rows grown in order under a forwarded-token budget (host)
  *   tree_pack_layout     parent array -> DFS slots, depth, subtree end, token_index (host)
  *   tree_rope            rotary embedding at depth, in place (device)
  *   tree_rope_qk         the same on q and k in one launch (device)
@@ -158,6 +159,36 @@ tree_status tree_place_leaves(int32_t n_nodes, const int32_t* parent, int32_t n_
                               const int32_t* seq_last, const int32_t* group, int32_t seq_len,
                               int32_t mode, int32_t* bin_of_seq, int32_t* bin_tokens,
                               int32_t bins_cap, int32_t* n_bins);
+
+/*
+ * tree_plan_rows - grow packed rows sample by sample under a budget of
+ * forwarded tokens (host, synchronous).
+ *
+ * [TRL "How tree packing works"]: the planner grows the trie sample by
+ * sample and its token_budget bounds unique (forwarded) tokens, not raw ones;
+ * [TRL "Limits and caveats to know before you switch"]: fork_threshold_tokens
+ * (1024 by default) sets how much prefix samples must have in common before
+ * they share it.  Samples are taken in input order; a sample joins the open
+ * row when the trie of the row plus the sample (tree_build_trie() with the
+ * fork threshold as its minimum shared run, default mode) holds at most
+ * token_budget nodes, else the open row is closed for good and the sample
+ * opens the next row.
+ *
+ *   n_seqs, seq_offsets, tokens   the samples, as for tree_build_trie()
+ *   fork_threshold_tokens  minimum common run that is shared (>= 0; 0 and 1 share any run)
+ *   token_budget  forwarded tokens a row may hold (>= 1); a sample longer than this is
+ *                 TREE_ERR_CAPACITY
+ *   row_of_seq    out [n_seqs] row of each sample
+ *   row_tokens    out [rows_cap] forwarded tokens of each row (NULL: not wanted)
+ *   n_rows        out: number of rows (written also on TREE_ERR_CAPACITY)
+ *   forked        out [n_seqs] 1 if the sample shares a slot with another sample of its row,
+ *                 else 0 (the per-sample flag behind [TRL "How to evaluate it on your own
+ *                 workload"]'s fork fraction); may be NULL
+ * TREE_ERR_CAPACITY when rows_cap < n_rows (row_of_seq is complete).
+ */
+tree_status tree_plan_rows(int32_t n_seqs, const int64_t* seq_offsets, const int32_t* tokens,
+                           int32_t fork_threshold_tokens, int64_t token_budget, int32_t* row_of_seq,
+                           int64_t* row_tokens, int32_t rows_cap, int32_t* n_rows, uint8_t* forked);
 
 /*
  * tree_pack_layout - lay one packed row out depth-first (host, synchronous).

@@ -135,3 +135,62 @@ def place_leaves(segs: Segments, group, seq_len: int, mode: str = "global") -> P
     else:
         raise ValueError(mode)
     return Placement(bin_of_seq=where, bin_tokens=np.asarray(bins_tok, dtype=np.int64))
+
+
+# ---------------------------------------------------------------------------
+# [TRL "How tree packing works"]: the planner grows the trie sample by sample,
+# and token_budget bounds a row's unique (forwarded) tokens, not its raw ones;
+# [TRL "Limits and caveats to know before you switch"]: fork_threshold_tokens
+# (1024 by default) decides how much of a prefix must be common before samples
+# share it.  Readings (listed in the design doc): samples are taken in arrival
+# order; a sample joins the open row when the trie of the row plus the sample
+# holds at most token_budget nodes, else the row is closed for good and the
+# sample opens the next one; the trie is the one of oracle.trie with the fork
+# threshold as its minimum shared run (a common run shorter than the
+# threshold is not shared; a shared one gives each branch its join copy); a
+# sample longer than token_budget is an error.  fork_frac is the share of
+# samples whose path shares a node with another sample of their row.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class GrownRows:
+    row_of_seq: np.ndarray         # [n_seqs] row of each sample
+    row_tokens: np.ndarray         # [n_rows] forwarded tokens (trie nodes) of each row
+    forked: np.ndarray             # [n_seqs] 1 if the sample shares a node with another sample of its row
+
+
+def grow_rows(sequences, token_budget: int, fork_threshold: int = 1024) -> GrownRows:
+    from .trie import build_trie
+
+    thr = max(1, int(fork_threshold))
+    n = len(sequences)
+    row_of = np.full(n, -1, dtype=np.int64)
+    rows: List[List[int]] = []
+    tokens: List[int] = []
+    cur: List[int] = []
+    cur_tokens = 0
+    for s in range(n):
+        if len(sequences[s]) > token_budget:
+            raise ValueError(f"sample {s} has {len(sequences[s])} tokens, more than the budget {token_budget}")
+        cand = cur + [s]
+        t = build_trie([sequences[i] for i in cand], min_shared=thr).n_nodes
+        if t <= token_budget:
+            cur, cur_tokens = cand, t
+        else:
+            rows.append(cur)
+            tokens.append(cur_tokens)
+            cur, cur_tokens = [s], len(sequences[s])
+    if cur:
+        rows.append(cur)
+        tokens.append(cur_tokens)
+    forked = np.zeros(n, dtype=np.int64)
+    for r, members in enumerate(rows):
+        row_of[members] = r
+        trie = build_trie([sequences[i] for i in members], min_shared=thr)
+        users = np.zeros(trie.n_nodes, dtype=np.int64)
+        for p in trie.paths:
+            users[np.unique(np.asarray(p, dtype=np.int64))] += 1
+        for k, i in enumerate(members):
+            p = np.asarray(trie.paths[k], dtype=np.int64)
+            forked[i] = int(len(p) > 0 and bool(np.any(users[p] > 1)))
+    return GrownRows(row_of_seq=row_of, row_tokens=np.asarray(tokens, dtype=np.int64), forked=forked)

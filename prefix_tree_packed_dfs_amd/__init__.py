@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     tree_gdn_workspace_bytes,
     tree_mfma_peak,
     tree_place_leaves,
+    tree_plan_rows,
     tree_pack_layout,
     tree_rope,
     tree_rope_qk,

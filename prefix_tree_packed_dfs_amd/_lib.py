@@ -56,6 +56,9 @@ lib.tree_build_trie.argtypes = [C.c_int32, _i64p, _i32p, C.POINTER(C.c_uint8), C
 lib.tree_place_leaves.restype = C.c_int
 lib.tree_place_leaves.argtypes = [C.c_int32, _i32p, C.c_int32, _i32p, _i32p, C.c_int32, C.c_int32, _i32p,
                                   _i32p, C.c_int32, _i32p]
+lib.tree_plan_rows.restype = C.c_int
+lib.tree_plan_rows.argtypes = [C.c_int32, _i64p, _i32p, C.c_int32, C.c_int64, _i32p, _i64p, C.c_int32, _i32p,
+                               C.POINTER(C.c_uint8)]
 lib.tree_pack_layout.restype = C.c_int
 lib.tree_pack_layout.argtypes = [C.c_int32, _i32p, C.c_int32, _i32p, C.c_int32, _i32p, _i32p, _i32p, _i64p,
                                  _i32p, C.c_int64]
@@ -96,7 +99,7 @@ lib.tree_mfma_peak.restype = C.c_int
 lib.tree_mfma_peak.argtypes = [C.c_int64, C.c_int64, _vp, C.POINTER(C.c_double), _vp]
 
 EXPORTED = ("tree_abi_version", "tree_status_string", "tree_last_error", "tree_build_trie",
-            "tree_place_leaves", "tree_pack_layout", "tree_validate_subtree_end", "tree_rope", "tree_rope_qk",
+            "tree_place_leaves", "tree_plan_rows", "tree_pack_layout", "tree_validate_subtree_end", "tree_rope", "tree_rope_qk",
             "tree_attn_workspace_bytes", "tree_attn_bwd_workspace_bytes_for",
             "tree_attn_fwd", "tree_attn_fwd_noalloc", "tree_attn_bwd", "tree_gdn_plan", "tree_gdn_workspace_bytes", "tree_gdn_fwd",
             "tree_mfma_peak")
@@ -161,6 +164,24 @@ def tree_place_leaves(parent, seq_last, group, seq_len: int, mode: str = "global
                                  None if grp is None else _ptr(grp, C.c_int32), int(seq_len), PLACE_MODES[mode],
                                  _ptr(bin_of, C.c_int32), _ptr(tokens, C.c_int32), cap, C.byref(n_bins)))
     return bin_of[:n].copy(), tokens[:n_bins.value].copy()
+
+
+def tree_plan_rows(sequences, token_budget: int, fork_threshold_tokens: int = 1024):
+    """Samples -> (row of each sample int32 [n_seqs], forwarded tokens per row int64 [n_rows],
+    forked flags uint8 [n_seqs]), rows grown in input order under the forwarded-token budget."""
+    seqs = [np.ascontiguousarray(s, dtype=np.int32) for s in sequences]
+    n = len(seqs)
+    offsets = np.zeros(n + 1, dtype=np.int64)
+    np.cumsum([len(s) for s in seqs], out=offsets[1:])
+    tokens = np.concatenate(seqs) if n and offsets[-1] else np.zeros(1, np.int32)
+    row_of = np.empty(max(n, 1), dtype=np.int32)
+    row_tok = np.empty(max(n, 1), dtype=np.int64)
+    forked = np.zeros(max(n, 1), dtype=np.uint8)
+    n_rows = C.c_int32(0)
+    _check(lib.tree_plan_rows(n, _ptr(offsets, C.c_int64), _ptr(tokens, C.c_int32), int(fork_threshold_tokens),
+                              int(token_budget), _ptr(row_of, C.c_int32), _ptr(row_tok, C.c_int64), max(n, 1),
+                              C.byref(n_rows), _ptr(forked, C.c_uint8)))
+    return row_of[:n].copy(), row_tok[:n_rows.value].copy(), forked[:n].copy()
 
 
 @dataclass

@@ -65,10 +65,12 @@ struct TrieBuilder {
     int32_t min_shared;
     std::vector<int32_t> parent;
     std::vector<int32_t> seq_last;
+    const int32_t* ids = nullptr;  // sequence s of this trie is input sequence ids[s] (NULL: s itself)
 
-    int64_t len(int32_t s) const { return off[s + 1] - off[s]; }
-    int32_t at(int32_t s, int64_t t) const { return tok[off[s] + t]; }
-    bool trained(int32_t s, int64_t t) const { return train && train[off[s] + t]; }
+    int64_t first(int32_t s) const { return off[ids ? ids[s] : s]; }
+    int64_t len(int32_t s) const { return off[(ids ? ids[s] : s) + 1] - first(s); }
+    int32_t at(int32_t s, int64_t t) const { return tok[first(s) + t]; }
+    bool trained(int32_t s, int64_t t) const { return train && train[first(s) + t]; }
 
     // One node per position in [start, end), shared by every sequence in `act`.
     int32_t emit(const std::vector<int32_t>& act, int64_t start, int64_t end, int32_t par) {
@@ -235,6 +237,91 @@ extern "C" tree_status tree_build_trie(int32_t n_seqs, const int64_t* seq_offset
         return fail(TREE_ERR_CAPACITY, "parent_cap %lld < %lld nodes", (long long)parent_cap,
                     (long long)tb.parent.size());
     if (!tb.parent.empty()) std::memcpy(parent, tb.parent.data(), sizeof(int32_t) * tb.parent.size());
+    return TREE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// tree_plan_rows
+// ---------------------------------------------------------------------------
+
+extern "C" tree_status tree_plan_rows(int32_t n_seqs, const int64_t* seq_offsets, const int32_t* tokens,
+                                      int32_t fork_threshold_tokens, int64_t token_budget, int32_t* row_of_seq,
+                                      int64_t* row_tokens, int32_t rows_cap, int32_t* n_rows, uint8_t* forked) {
+    treeattn::clear_error();
+    if (n_seqs < 0) return fail(TREE_ERR_INVALID_ARG, "n_seqs = %d < 0", n_seqs);
+    if (!n_rows) return fail(TREE_ERR_INVALID_ARG, "n_rows is NULL");
+    if (fork_threshold_tokens < 0) return fail(TREE_ERR_INVALID_ARG, "fork_threshold_tokens = %d < 0",
+                                               fork_threshold_tokens);
+    if (token_budget < 1) return fail(TREE_ERR_INVALID_ARG, "token_budget = %lld < 1", (long long)token_budget);
+    if (rows_cap < 0) return fail(TREE_ERR_INVALID_ARG, "rows_cap < 0");
+    if (n_seqs > 0 && (!seq_offsets || !row_of_seq))
+        return fail(TREE_ERR_INVALID_ARG, "seq_offsets or row_of_seq is NULL");
+    if (n_seqs > 0 && seq_offsets[0] != 0) return fail(TREE_ERR_INVALID_ARG, "seq_offsets[0] != 0");
+    for (int32_t s = 0; s < n_seqs; ++s)
+        if (seq_offsets[s + 1] < seq_offsets[s])
+            return fail(TREE_ERR_INVALID_ARG, "seq_offsets decreases at %d", s);
+    const int64_t total = n_seqs > 0 ? seq_offsets[n_seqs] : 0;
+    if (total > 0 && !tokens) return fail(TREE_ERR_INVALID_ARG, "tokens is NULL");
+    if (total > INT32_MAX) return fail(TREE_ERR_UNSUPPORTED, "more than 2^31-1 tokens");
+    for (int32_t s = 0; s < n_seqs; ++s)
+        if (seq_offsets[s + 1] - seq_offsets[s] > token_budget)
+            return fail(TREE_ERR_CAPACITY, "sample %d has %lld tokens, more than token_budget %lld", s,
+                        (long long)(seq_offsets[s + 1] - seq_offsets[s]), (long long)token_budget);
+
+    // Forwarded tokens of the trie over `members` (node count), and, when
+    // wanted, which members share a node with another member.
+    const int32_t thr = std::max<int32_t>(1, fork_threshold_tokens);
+    auto trie_of = [&](const std::vector<int32_t>& members, std::vector<uint8_t>* shares) -> int64_t {
+        TrieBuilder tb{seq_offsets, tokens, nullptr, thr, {}, {}};
+        tb.ids = members.data();
+        tb.seq_last.assign(members.size(), -1);
+        tb.run((int32_t)members.size());
+        if (shares) {
+            std::vector<int32_t> users(tb.parent.size(), 0);
+            for (int32_t v : tb.seq_last)
+                for (int32_t x = v; x >= 0; x = tb.parent[x]) ++users[x];
+            shares->assign(members.size(), 0);
+            for (size_t i = 0; i < members.size(); ++i)
+                for (int32_t x = tb.seq_last[i]; x >= 0; x = tb.parent[x])
+                    if (users[x] > 1) {
+                        (*shares)[i] = 1;
+                        break;
+                    }
+        }
+        return (int64_t)tb.parent.size();
+    };
+
+    int32_t rows = 0;
+    std::vector<int32_t> cur;
+    int64_t cur_tokens = 0;
+    auto close_row = [&]() {
+        if (cur.empty()) return;
+        if (rows < rows_cap && row_tokens) row_tokens[rows] = cur_tokens;
+        if (forked) {
+            std::vector<uint8_t> sh;
+            trie_of(cur, &sh);
+            for (size_t i = 0; i < cur.size(); ++i) forked[cur[i]] = sh[i];
+        }
+        for (int32_t s : cur) row_of_seq[s] = rows;
+        ++rows;
+        cur.clear();
+    };
+    for (int32_t s = 0; s < n_seqs; ++s) {
+        cur.push_back(s);
+        const int64_t t = trie_of(cur, nullptr);
+        if (t <= token_budget) {
+            cur_tokens = t;
+            continue;
+        }
+        cur.pop_back();
+        close_row();
+        cur.push_back(s);
+        cur_tokens = seq_offsets[s + 1] - seq_offsets[s];
+    }
+    close_row();
+    *n_rows = rows;
+    if (rows > rows_cap && row_tokens)
+        return fail(TREE_ERR_CAPACITY, "rows_cap %d < %d rows", rows_cap, rows);
     return TREE_OK;
 }
 

@@ -64,3 +64,62 @@ def test_placement_errors():
         lib.tree_place_leaves(parent, seq_last, None, 100, "global")   # groups required
     b, t = lib.tree_place_leaves(parent, seq_last, None, 100, "in_order")
     assert b.tolist() == [0] and t.tolist() == [50]
+
+
+# ---------------------------------------------------------------------------
+# tree_plan_rows: TRL's planner (rows grown sample by sample under a budget of forwarded tokens)
+# ---------------------------------------------------------------------------
+
+from oracle.pack import grow_rows  # noqa: E402
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_plan_rows_matches_oracle(seed):
+    rng = np.random.default_rng(1300 + seed)
+    seqs, _ = _random_forest(rng, int(rng.integers(1, 30)), vocab=int(rng.integers(2, 4)), max_len=60)
+    budget = max(len(s) for s in seqs) + int(rng.integers(0, 200))
+    for thr in (0, 1, 4, 9, 1024):
+        ref = grow_rows(seqs, token_budget=budget, fork_threshold=thr)
+        row_of, row_tok, forked = lib.tree_plan_rows(seqs, budget, thr)
+        assert np.array_equal(row_of, ref.row_of_seq)
+        assert np.array_equal(row_tok, ref.row_tokens)
+        assert np.array_equal(forked, ref.forked)
+
+
+def test_plan_rows_workloads_match_oracle():
+    """grpo_group's 16 rollouts and long_history's 8 under budgets that split them, both thresholds."""
+    from synth import grpo_group, long_history
+    for w, budgets in ((grpo_group(), (18_447, 10_000, 6_000)), (long_history(), (36_864, 30_000))):
+        for thr in (64, 1024, 4096):
+            for budget in budgets:
+                ref = grow_rows(w.sequences, token_budget=budget, fork_threshold=thr)
+                row_of, row_tok, forked = lib.tree_plan_rows(w.sequences, budget, thr)
+                assert np.array_equal(row_of, ref.row_of_seq) and np.array_equal(row_tok, ref.row_tokens)
+                assert np.array_equal(forked, ref.forked)
+
+
+def test_plan_rows_errors():
+    import ctypes as C
+    L = lib.lib
+    with pytest.raises(lib.TreeAttnError) as e:
+        lib.tree_plan_rows([[1, 2, 3], list(range(50))], 40)
+    assert e.value.status == 3
+    with pytest.raises(lib.TreeAttnError) as e:
+        lib.tree_plan_rows([[1, 2]], 0)
+    assert e.value.status == 1
+    with pytest.raises(lib.TreeAttnError) as e:
+        lib.tree_plan_rows([[1, 2]], 10, -1)
+    assert e.value.status == 1
+    # fewer row slots than rows: TREE_ERR_CAPACITY, the row count and every sample's row still written
+    seqs = [np.arange(10 * i, 10 * i + 8, dtype=np.int32) for i in range(5)]
+    offs = np.zeros(6, np.int64)
+    np.cumsum([8] * 5, out=offs[1:])
+    toks = np.concatenate(seqs)
+    row_of = np.full(5, -7, np.int32)
+    row_tok = np.zeros(2, np.int64)
+    n = C.c_int32(0)
+    i32, i64 = C.POINTER(C.c_int32), C.POINTER(C.c_int64)
+    st = L.tree_plan_rows(5, offs.ctypes.data_as(i64), toks.ctypes.data_as(i32), 1024, 16, row_of.ctypes.data_as(i32),
+                          row_tok.ctypes.data_as(i64), 2, C.byref(n), None)
+    assert st == 3 and n.value == 3 and row_of.tolist() == [0, 0, 1, 1, 2]
+    assert lib.tree_plan_rows([], 10)[1].size == 0

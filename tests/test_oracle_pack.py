@@ -187,3 +187,108 @@ def test_too_long_sequence_is_an_error():
     tr = build_trie([np.arange(50)], min_shared=1)
     with pytest.raises(ValueError):
         place_leaves(segments(tr.parent, tr.seq_last), [0], 49, "global")
+
+
+# ---------------------------------------------------------------------------
+# TRL's planner: rows grown sample by sample under a forwarded-token budget
+# ---------------------------------------------------------------------------
+
+from oracle.pack import grow_rows  # noqa: E402
+
+TRL_DOCS = os.path.join(os.path.dirname(__file__), "golden", "trl_docs_example.json")
+TRL_ENVELOPE = os.path.join(os.path.dirname(__file__), "golden", "trl_back_of_envelope.json")
+
+
+def _docs_rollouts():
+    g = json.load(open(TRL_DOCS))
+    per = g["raw_tokens"] // g["rollouts"]
+    prompt = list(range(1, g["prompt_tokens"] + 1))
+    return g, [prompt + [100 * (r + 1) + t for t in range(per - g["prompt_tokens"])] for r in range(g["rollouts"])]
+
+
+def test_grow_rows_docs_example_and_fork_threshold():
+    """[TRL "How tree packing works"]: 10 raw tokens, 8 forwarded once the 3-token prompt is shared
+    (a fork threshold of at most 3); with the default threshold of 1024 the prompt is too short to
+    share and all 10 are forwarded."""
+    g, seqs = _docs_rollouts()
+    for thr in (0, 1, 3):
+        r = grow_rows(seqs, token_budget=100, fork_threshold=thr)
+        assert r.row_tokens.tolist() == [g["forwarded_tokens"]] and r.forked.tolist() == [1, 1]
+    for thr in (4, 1024):
+        r = grow_rows(seqs, token_budget=100, fork_threshold=thr)
+        assert r.row_tokens.tolist() == [g["raw_tokens"]] and r.forked.tolist() == [0, 0]
+    # the budget bounds forwarded tokens: 8 fit a budget of 8 when shared, 10 do not
+    assert grow_rows(seqs, token_budget=8, fork_threshold=1).row_of_seq.tolist() == [0, 0]
+    assert grow_rows(seqs, token_budget=8, fork_threshold=1024).row_of_seq.tolist() == [0, 1]
+
+
+def test_grow_rows_back_of_envelope_history():
+    """[TRL "A back-of-envelope example"]: a 20,000-token history and 8 rollouts of 2,000 own tokens.
+    With the default threshold the history is shared: k rollouts in a row forward 19,999 + 2,001 k
+    tokens (one join copy per branch), so a 36,864-token budget holds all eight (36,007) and a budget
+    of 36,006 closes the row after seven (34,006), the eighth opening a row of its own (22,000)."""
+    g = json.load(open(TRL_ENVELOPE))
+    H, n, u = g["history_tokens"], g["rollouts"], g["new_tokens"]
+    hist = list(range(H))
+    seqs = [hist + list(range(10 ** 6 * (r + 1), 10 ** 6 * (r + 1) + u)) for r in range(n)]
+    r = grow_rows(seqs, token_budget=36864, fork_threshold=1024)
+    assert r.row_tokens.tolist() == [H - 1 + n * (u + 1)] and set(r.forked.tolist()) == {1}
+    r = grow_rows(seqs, token_budget=H - 1 + n * (u + 1) - 1, fork_threshold=1024)
+    assert r.row_tokens.tolist() == [H - 1 + (n - 1) * (u + 1), H + u]
+    assert r.row_of_seq.tolist() == [0] * (n - 1) + [1] and r.forked.tolist() == [1] * (n - 1) + [0]
+    assert sum(len(s) for s in seqs) == g["raw_tokens"]
+
+
+def _next_fit(lengths, cap):
+    """Textbook next-fit bin packing: items in order, a new bin when the next item does not fit."""
+    bins, loads = [], []
+    for L in lengths:
+        if not loads or loads[-1] + L > cap:
+            loads.append(0)
+        loads[-1] += L
+        bins.append(len(loads) - 1)
+    return bins, loads
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_grow_rows_without_sharing_is_next_fit(seed):
+    """Samples with nothing in common (or a threshold above every common run) forward their raw tokens,
+    so growing rows in order reduces to next-fit bin packing on the sample lengths."""
+    rng = np.random.default_rng(70 + seed)
+    lens = rng.integers(1, 60, int(rng.integers(1, 30)))
+    seqs = [list(range(10_000 * i, 10_000 * i + int(L))) for i, L in enumerate(lens)]
+    cap = int(lens.max()) + int(rng.integers(0, 100))
+    bins, loads = _next_fit(lens, cap)
+    r = grow_rows(seqs, token_budget=cap, fork_threshold=1)
+    assert r.row_of_seq.tolist() == bins and r.row_tokens.tolist() == loads and not r.forked.any()
+    shared = [[7] * 5 + s for s in seqs]          # a 5-token common run, below a threshold of 6
+    bins, loads = _next_fit(lens + 5, cap + 5)
+    r = grow_rows(shared, token_budget=cap + 5, fork_threshold=6)
+    assert r.row_of_seq.tolist() == bins and r.row_tokens.tolist() == loads
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_grow_rows_invariants(seed):
+    """Rows are runs of consecutive samples; each holds the trie of its samples, within the budget; a
+    row is closed only when the next sample would not fit; a sample alone in its row has not forked."""
+    rng = np.random.default_rng(300 + seed)
+    seqs, _ = _random_forest(rng, int(rng.integers(1, 25)), vocab=int(rng.integers(2, 4)))
+    budget = max(len(s) for s in seqs) + int(rng.integers(0, 120))
+    thr = int(rng.integers(0, 20))
+    r = grow_rows(seqs, token_budget=budget, fork_threshold=thr)
+    row = r.row_of_seq
+    assert row[0] == 0 and np.all(np.diff(row) >= 0) and np.all(np.diff(row) <= 1)
+    for k in range(len(r.row_tokens)):
+        members = np.nonzero(row == k)[0]
+        t = build_trie([seqs[i] for i in members], min_shared=max(1, thr)).n_nodes
+        assert t == r.row_tokens[k] <= budget
+        if k + 1 < len(r.row_tokens):
+            nxt = int(np.nonzero(row == k + 1)[0][0])
+            assert build_trie([seqs[i] for i in list(members) + [nxt]], min_shared=max(1, thr)).n_nodes > budget
+        if len(members) == 1:
+            assert r.forked[members[0]] == 0
+
+
+def test_grow_rows_rejects_a_sample_beyond_the_budget():
+    with pytest.raises(ValueError):
+        grow_rows([[1, 2, 3], list(range(50))], token_budget=40)
