@@ -31,6 +31,7 @@ WORKLOADS = {
     "long_history": 5,
 }
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 COPY_BYTES = 1 << 30         # size of the plain copy used to calibrate the HBM byte counters
 
 
@@ -81,6 +82,75 @@ def describe(w, n, R, pairs):
     }
 
 
+def row_counts(w, lay, n, R):
+    """[TRL "How to evaluate it on your own workload"]: packing ratio, fork fraction (share of sequences
+    whose path shares a slot with another sequence) and row fill (forwarded / row slots), from the
+    library's layout."""
+    import numpy as np
+    users = np.zeros(R, np.int64)
+    paths = [lay.sequence_slots(s) for s in range(len(w.sequences))]
+    for p in paths:
+        users[np.unique(p)] += 1
+    forked = sum(1 for p in paths if len(p) and bool((users[p] > 1).any()))
+    return {"packing_ratio": round(w.raw_tokens / n, 4), "fork_frac": round(forked / max(len(paths), 1), 4),
+            "row_fill": round(n / R, 4)}
+
+
+def tile_classes(w, se, R):
+    """The forward's tile classes per KV head: every (query block, 64-key tile) pair of a block's visible
+    range, as the kernels classify them from per-tile min / max subtree_end (skipped: no key of the tile
+    sees the block; full: every key sees every query; partial: the interval test runs per element).
+    Query blocks are the kernels' items (256 rows = BM positions x HB query heads sharing a KV head);
+    blocks of isolated slots only (padding) are left to the isolated-slot units and not counted."""
+    import numpy as np
+    G = w.Hq // w.Hkv
+    HB = 8 if G >= 8 else G
+    BM, KT = 256 // HB, 64
+    T = (R + KT - 1) // KT
+    pad = np.concatenate([se, np.full(T * KT - R, -1, np.int64)])
+    idx = np.arange(T * KT)
+    tmax = pad.reshape(T, KT).max(axis=1)
+    tmin = np.where(idx < R, pad, np.iinfo(np.int64).max).reshape(T, KT).min(axis=1)
+    self_only = np.all(((pad == idx) | (idx >= R)).reshape(T, KT), axis=1)
+    before = np.concatenate([[-1], np.maximum.accumulate(tmax)[:-1]])
+    iso = self_only & (before < np.arange(T) * KT)
+    full = partial = skipped = blocks = 0
+    for qb in range((R + BM - 1) // BM):
+        i0, i1 = qb * BM, min(qb * BM + BM, R) - 1
+        t_last = i1 // KT
+        if iso[i0 // KT:t_last + 1].all():
+            continue
+        blocks += 1
+        t = np.arange(t_last + 1)
+        vis = tmax[:t_last + 1] >= i0
+        f = vis & (t * KT + KT - 1 <= i0) & (tmin[:t_last + 1] >= i1)
+        full += int(f.sum())
+        partial += int((vis & ~f).sum())
+        skipped += int((~vis).sum())
+    chunks = G // HB
+    return {"query_blocks": blocks * chunks, "full": full * chunks, "partial": partial * chunks,
+            "skipped": skipped * chunks, "block_rows": BM, "key_tile": KT}
+
+
+def algorithmic_bytes(w, n):
+    """What the path must move per call (bf16 / fp32 elements, fp32 lse and delta): forward reads q, k, v
+    and writes out, lse; backward reads q, k, v, out, dout, lse, reads and writes delta, writes dq, dk, dv."""
+    e = 2 if w.dtype == "bf16" else 4
+    fwd = n * ((w.Hq + 2 * w.Hkv) * w.D * e + w.Hq * w.D * e + 4 * w.Hq)
+    bwd = n * (2 * (w.Hq + 2 * w.Hkv) * w.D * e + 2 * w.Hq * w.D * e + 8 * w.Hq)
+    return fwd, bwd
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, total_flops, target_s):
     """Time the oracle (fwd + bwd, fp64, CPU) on the first sequences of the workload."""
     import numpy as np
@@ -102,6 +172,9 @@ def cpu_baseline(w, total_flops, target_s):
             break
         k = min(len(w.sequences), max(k + 1, int(k * (target_s / 4) / max(dt, 1e-3))))
     raw_k = sum(len(s) for s in seqs)
+    t0 = time.perf_counter()
+    tree_attention(seqs, w.fid[:k], w.dkey[:k], tables, theta=w.theta, backward=False, storage=w.dtype)
+    dt_fwd = time.perf_counter() - t0
     # the oracle's cost is per unpacked sequence: extrapolate by raw-token work share
     work = lambda ss: sum(len(s) * (len(s) + 1) / 2 for s in ss)  # noqa: E731
     frac = work(seqs) / work(w.sequences)
@@ -114,9 +187,14 @@ def cpu_baseline(w, total_flops, target_s):
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"oracle fwd+bwd on the first {k} of {len(w.sequences)} sequences ({raw_k} of {raw_all} raw "
-                  f"tokens, {frac:.3f} of the oracle's per-sequence work) took {dt:.2f} s; whole-row time "
-                  f"extrapolated to {full_s:.1f} s",
+                  f"tokens, {frac:.3f} of the oracle's per-sequence work) took {dt:.2f} s (forward alone "
+                  f"{dt_fwd:.2f} s); whole-row time extrapolated to {full_s:.1f} s",
         "seconds_sample": round(dt, 3),
+        "seconds_sample_fwd": round(dt_fwd, 3),
+        "raw_tok_s_sample": round(raw_k / dt, 1),
+        "raw_tok_s_sample_fwd": round(raw_k / dt_fwd, 1),
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
     }
 
 
@@ -476,7 +554,8 @@ def main():
     se_d = torch.empty((1, R), device=dev, dtype=torch.int32)
     wsf = torch.empty(max(lib.tree_attn_workspace_bytes(dt_code, 1, R, w.Hq, w.Hkv, w.D, False), 1),
                       device=dev, dtype=torch.uint8)
-    wsb = torch.empty(max(lib.tree_attn_workspace_bytes(dt_code, 1, R, w.Hq, w.Hkv, w.D, True), 1),
+    # the backward workspace this row's dK/dV plan uses (fixed part + its partial-sum slots)
+    wsb = torch.empty(max(lib.tree_attn_bwd_workspace_bytes_for(dt_code, lay.subtree_end, w.Hq, w.Hkv, w.D), 1),
                       device=dev, dtype=torch.uint8)
 
     # pinned, double-buffered host layout buffers
@@ -565,6 +644,26 @@ def main():
 
     value = total_flops / (ms_step * 1e-3) / 1e12
     bwd_tf = bwd_flops / (bwd_ms * 1e-3) / 1e12
+    fwd_bytes, bwd_bytes = algorithmic_bytes(w, n)
+    fwd_gbs = fwd_bytes / (fwd_ms * 1e-3) / 1e9
+    bwd_gbs = bwd_bytes / (bwd_ms * 1e-3) / 1e9
+    traffic = measured_traffic(w.name)
+    # matrix-core bound unless the row's algorithmic flop per byte is below the machine balance
+    # (2.5 PFLOP/s / 8 TB/s), as for independent short sequences
+    hbm_bound = (fwd_flops + bwd_flops) / (fwd_bytes + bwd_bytes) < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm_bound:
+        roofline = {"kernel": "tree_attn_bwd (every kernel of the call)", "bound": "hbm",
+                    "achieved": round(bwd_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(bwd_gbs / PEAK_HBM_GBS, 4)}
+    else:
+        roofline = {"kernel": "tree_attn_bwd (every kernel of the call)", "bound": "mfma",
+                    "achieved": round(bwd_tf, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4)}
+    roofline["traffic"] = traffic
+    roofline["traffic_source"] = (f"profiles/{w.name}_traffic.md: rocprofv3 FETCH_SIZE and WRITE_SIZE of every "
+                                  "backward kernel, scaled by a plain copy, taken on these kernel sources "
+                                  "(not measured in this run)") if traffic is not None else None
+    roofline["algorithmic_bytes"] = int(bwd_bytes)
     rec = {
         "metric": "tree-attn fwd+bwd ancestor-pair TFLOP/s & forwarded tok/s, 32K row, 1 GPU",
         "value": round(value, 3),
@@ -589,15 +688,12 @@ def main():
         "measured_mfma_peak_tflops": round(measured_peak, 1),
         "frac_of_measured_peak_step": round(value / measured_peak, 4),
         "cold_ms_per_step": round(float(np.median(cold)), 4),
-        "roofline": {
-            "kernel": "tree_attn_bwd (every kernel of the call)",
-            "bound": "mfma",
-            "achieved": round(bwd_tf, 3),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(w.name),
-        },
+        "counts": row_counts(w, lay, n, R),
+        "tiles_per_kv_head": tile_classes(w, lay.subtree_end.astype(np.int64), R),
+        "hbm_gbs": {"fwd": round(fwd_gbs, 1), "bwd": round(bwd_gbs, 1),
+                    "algorithmic_bytes_fwd": int(fwd_bytes), "algorithmic_bytes_bwd": int(bwd_bytes)},
+        "bwd_workspace_bytes": int(wsb.numel()),
+        "roofline": roofline,
         "source_hash": source_hash(),
     }
     if not args.no_cpu_baseline:
