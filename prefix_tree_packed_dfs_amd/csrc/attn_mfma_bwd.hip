@@ -624,6 +624,8 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
     static_assert(2 * PER_TILE < 16, "wait counts");
     constexpr int LCAP = 1024;
     constexpr int FULL = 1 << 30;
+    // LDS operand loads in flight ahead of the products that read them
+    constexpr int PF_KV = 2, PF_TR = 3;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: load bases stay scalar
@@ -718,18 +720,11 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
         const int ln = lane_id_here();
         if (ln < 8) dma4s(seb + j0, (uint32_t)min(wave * 8 + ln, lim) * 4u, dst + 2 * KBYTES + wave * 32);
     };
-    // operand loads of K / V rows: row x * 32 + l32, chunk 2c + hi
-    const int nat_x = (hi ^ row_swizzle<D>(l32)) * 16;
-    // transposed loads of K rows for the K^T operand (lane mapping as in the dK/dV kernel)
-    int tr_off[NDB][2];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int row = 4 * (lane >> 5) + ((lane >> 2) & 3) + 8 * half;
-            const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-            tr_off[db][half] = row * KROW + ((chunk ^ row_swizzle<D>(row)) * 16) + 8 * (lane & 1);
-        }
+    // operand loads of K / V rows: row x * 32 + l32, chunk 2c + hi (chunk 0's
+    // offset here; chunk c is that XOR 32 c), and the transposed loads of K rows
+    // for the K^T operand
+    const uint32_t o_nat = (uint32_t)(l32 * KROW + ((hi ^ row_swizzle<D>(l32)) * 16));
+    const uint32_t o_tr = tr_offset0<D>(lane);
 
     int resume = 0;
     while (resume >= 0) {
@@ -780,13 +775,25 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
                 f32x16 sacc, dpt;
                 zero(sacc);
                 zero(dpt);
-                const int row = x * 32 + l32;
+                // K and V chunks of rows x * 32 + l32, PF_KV chunks ahead of the products
+                const uint32_t kv = lds_off(st) + (uint32_t)(x * 32 * KROW) + o_nat;
+                bf16x8 kq[PF_KV], vq[PF_KV];
+#pragma unroll
+                for (int i = 0; i < PF_KV; ++i) {
+                    kq[i] = lds_ld16(kv ^ (32u * i));
+                    vq[i] = lds_ld16((kv ^ (32u * i)) + KBYTES);
+                }
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    const int o = row * KROW + ((32 * c) ^ nat_x);
-                    sacc = mfma32(ld16<bf16x8>(st + o), qf[c], sacc);
-                    dpt = mfma32(ld16<bf16x8>(st + KBYTES + o), df[c], dpt);
-                    if (c % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+                    const bf16x8 ka = kq[c % PF_KV], va = vq[c % PF_KV];
+                    if (c + PF_KV < NC) {
+                        const uint32_t a = kv ^ (32u * (c + PF_KV));
+                        kq[c % PF_KV] = lds_ld16(a);
+                        vq[c % PF_KV] = lds_ld16(a + KBYTES);
+                    }
+                    sacc = mfma32(ka, qf[c], sacc);
+                    dpt = mfma32(va, df[c], dpt);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 float p[16];
 #pragma unroll
@@ -806,14 +813,20 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
                 bf16x8 dsf[2];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dsf[r >> 3][r & 7] = (__bf16)(p[r] * (dpt[r] - dlq));
-                // dQ^T += K^T dS^T (K^T by transposed loads of the K rows)
+                // dQ^T += K^T dS^T (K^T by transposed loads of the K rows, PF_TR steps ahead)
+                const uint32_t tk = lds_off(st) + (uint32_t)(x * 32 * KROW) + o_tr;
+                bf16x8 tq[PF_TR];
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+                for (int i = 0; i < PF_TR; ++i) tq[i] = lds_tr_block<D>(tk, i >> 1, 16 * (i & 1));
 #pragma unroll
-                    for (int c2 = 0; c2 < 2; ++c2) {
-                        const char* r0 = st + (x * 32 + c2 * 16) * KROW;
-                        acc[db] = mfma32(ld_tr(r0 + tr_off[db][0], r0 + tr_off[db][1]), dsf[c2], acc[db]);
-                    }
+                for (int step = 0; step < 2 * NDB; ++step) {
+                    const int db = step >> 1, c2 = step & 1;
+                    const bf16x8 ta = tq[step % PF_TR];
+                    if (step + PF_TR < 2 * NDB)
+                        tq[step % PF_TR] = lds_tr_block<D>(tk, (step + PF_TR) >> 1, 16 * ((step + PF_TR) & 1));
+                    acc[db] = mfma32(ta, dsf[c2], acc[db]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 // keep the two key halves apart: interleaving them needs more
                 // registers than a wave has
                 __builtin_amdgcn_sched_barrier(0);

@@ -61,6 +61,40 @@ __device__ __forceinline__ bf16x8 ld_tr(const void* lo, const void* hi) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// LDS loads at 32-bit LDS offsets.  With rows of a multiple of 128 bytes at
+// 256-byte aligned bases and chunks swizzled only in bits 4-7, the address of
+// chunk c of a row is (base + this lane's chunk-0 offset) XOR 32 c, and row
+// blocks, halves and arrays are immediate offsets: one register per array
+// instead of one per chunk.
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+__device__ __forceinline__ uint32_t lds_off(const void* p) { return (uint32_t)(uintptr_t)(const lds_char_t*)p; }
+__device__ __forceinline__ bf16x8 lds_ld16(uint32_t a) { return *(lds_bf16x8_t*)a; }
+__device__ __forceinline__ bf16x8 lds_ld_tr(uint32_t lo, uint32_t hi) {
+    const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)lo);
+    const bf16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)hi);
+    return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// Transposed-load offset of this lane for head-dim block 0, first half: the
+// lane supplies row 4 (lane / 32) + (lane / 4) % 4 (+ 8 for slots 4-7) and
+// column 16 ((lane / 16) % 2) + 4 (lane % 4) (+ 32 per head-dim block).  Block
+// db, half h is (offset XOR (64 db + 32 h)) + 8 h rows.
+template <int D>
+__device__ __forceinline__ uint32_t tr_offset0(int lane) {
+    constexpr int ROWB = D * 2;
+    const int row = 4 * (lane >> 5) + ((lane >> 2) & 3);
+    const int chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    return (uint32_t)(row * ROWB + ((chunk ^ row_swizzle<D>(row)) * 16) + 8 * (lane & 1));
+}
+// The transposed operand of 16 rows starting `rows16` rows into the array at
+// LDS offset `base` (= array start + tr_offset0), head-dim block db.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr_block(uint32_t base, int db, int rows16) {
+    constexpr int ROWB = D * 2;
+    return lds_ld_tr((base ^ (64u * db)) + rows16 * ROWB, (base ^ (64u * db + 32u)) + rows16 * ROWB + 8 * ROWB);
+}
+
 // First tile index >= from (and <= t_last) whose largest subtree_end reaches
 // i0; -1 if none.  Wave-uniform: 64 tiles are tested per step with one ballot.
 __device__ __forceinline__ int next_visible(const int32_t* __restrict__ tmaxb, int from, int t_last, int i0) {
