@@ -355,6 +355,38 @@ def test_backward_workspace_exact_size_gives_the_same_results():
         assert e <= 1e-2
 
 
+@pytest.mark.gpu
+def test_backward_reads_no_workspace_it_did_not_write():
+    """grpo_group at full size (its padding rows after the last real keys included): the backward
+    with its workspace filled with zeros and with 0xFF bytes (NaN as fp32) before the call gives
+    bitwise the same dq, dk, dv, so every workspace word a kernel reads was written in the call."""
+    import torch
+
+    import prefix_tree_packed_dfs_amd as lib
+    w = standard(2)
+    log(f"case workspace contents: {w.name} Hq={w.Hq} Hkv={w.Hkv} D={w.D}")
+    parent, seq_last = lib.tree_build_trie(w.sequences, min_shared=64)
+    n = len(parent)
+    R = w.row_length(n)
+    assert R - n >= 256, "the row needs padding past a 256-key tile"
+    lay = lib.tree_pack_layout(parent, seq_last, R)
+    se = torch.from_numpy(lay.subtree_end.astype(np.int32)).view(1, R).cuda()
+    g = torch.Generator().manual_seed(13)
+    mk = lambda H: torch.randn(1, R, H, w.D, generator=g).to(torch.bfloat16).cuda()  # noqa: E731
+    q, k, v, do = mk(w.Hq), mk(w.Hkv), mk(w.Hkv), mk(w.Hq)
+    out, lse = lib.tree_attn_fwd(q, k, v, se)
+    nbytes = lib.tree_attn_bwd_workspace_bytes_for(lib.TREE_BF16, lay.subtree_end.astype(np.int32), w.Hq,
+                                                   w.Hkv, w.D)
+    res = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+        res.append(lib.tree_attn_bwd(q, k, v, se, out, lse, do, ws=ws))
+        torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), res[0], res[1]):
+        assert torch.isfinite(a.float()).all(), name
+        assert torch.equal(a, b), name
+
+
 def test_outputs_stay_inside_their_buffers():
     """Guard bands of sentinel values before and after out, lse, dq, dk, dv and both workspaces
     (grpo_group at full size, each buffer a view into a larger one): after the forward and the
