@@ -445,15 +445,40 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
     const float* rowvec = wave < 4 ? lse2 : delta;
 
     // all of this wave's loads for one visit (32 positions x one query head)
-    auto issue = [&](int vl, int stage) {
-        char* dst = smem + stage * STAGE;
+    // Visit v of the unit covers positions (pb0 + (v_begin + v) / G) * 32 on
+    // query head g * G + (v_begin + v) % G.  The loads and the products step
+    // through the visits with a cursor each (block, head in the group, and
+    // the element offsets of the rows): no division per visit.
+    struct Cursor {
+        int blk, hh;
+        int64_t qoff, roff;  // Q / dout rows, lse2 / delta rows
+    };
+    auto cursor_at = [&](int vl) {
         const int vi = v_begin + vl;
-        const int i0 = (pb0 + vi / G) * 32;
-        const int h = g * G + vi % G;
+        Cursor c;
+        c.blk = pb0 + vi / G;
+        c.hh = vi % G;
+        c.qoff = (((int64_t)b * N + c.blk * 32) * Hq + g * G + c.hh) * D;
+        c.roff = ((int64_t)b * Hq + g * G + c.hh) * N + c.blk * 32;
+        return c;
+    };
+    auto advance = [&](Cursor& c) {
+        if (++c.hh == G) {
+            c.hh = 0;
+            ++c.blk;
+            c.qoff += (int64_t)(32 * Hq - (G - 1)) * D;
+            c.roff += 32 - (int64_t)(G - 1) * N;
+        } else {
+            c.qoff += D;
+            c.roff += N;
+        }
+    };
+    auto issue = [&](const Cursor& c, int stage) {
+        char* dst = smem + stage * STAGE;
+        const int i0 = c.blk * 32;
         const int lim = N - 1 - i0;  // rows past the end repeat the last one
-        const int64_t base = (((int64_t)b * N + i0) * Hq + h) * D;
-        const __bf16* qb = q + base;
-        const __bf16* db = dout + base;
+        const __bf16* qb = q + c.qoff;
+        const __bf16* db = dout + c.qoff;
 #pragma unroll
         for (int u = 0; u < NDMA; ++u) {
             const int e0 = wave * NCH + u * 64;  // first chunk of this load
@@ -465,7 +490,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
         }
         const int ln = lane_id_here();
         if (ln < 8) {
-            const float* rb = rowvec + ((int64_t)b * Hq + h) * N + i0;
+            const float* rb = rowvec + c.roff;
             dma4s(rb, (uint32_t)min((wave & 3) * 8 + ln, lim) * 4u, dst + 2 * NBYTES + wave * 32);
         }
     };
@@ -543,9 +568,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
         }
     };
 
+    Cursor ic = cursor_at(0);  // next visit to load
 #pragma unroll
     for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
-        if (s0 < nvis) issue(s0, s0);
+        if (s0 < nvis) {
+            issue(ic, s0);
+            advance(ic);
+        }
+    Cursor cc = cursor_at(0);  // visit of the products
     for (int vi = 0; vi < nvis; ++vi) {
         // visits issued after this one and possibly still in flight
         const int ahead = min(nvis - 1 - vi, NSTAGE - 2);
@@ -553,8 +583,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
         else if (ahead == 1) wait_vmcnt<PER_VISIT>();
         else wait_vmcnt<0>();
         barrier();
-        if (vi + NSTAGE - 1 < nvis) issue(vi + NSTAGE - 1, (vi + NSTAGE - 1) % NSTAGE);
-        const int i_lo = (pb0 + (v_begin + vi) / G) * 32;
+        if (vi + NSTAGE - 1 < nvis) {
+            issue(ic, (vi + NSTAGE - 1) % NSTAGE);
+            advance(ic);
+        }
+        const int i_lo = cc.blk * 32;
+        advance(cc);
         const bool skip = (j0w > i_lo + 31) || (wmax < i_lo);
         if (skip) continue;
         const bool full = (j0w + 31 <= i_lo) && (wmin >= i_lo + 31);
