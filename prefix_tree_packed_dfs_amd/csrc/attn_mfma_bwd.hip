@@ -811,6 +811,10 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
                 zero(dpt);
                 // K and V chunks of rows x * 32 + l32, PF_KV chunks ahead of the products
                 const uint32_t kv = lds_off(st) + (uint32_t)(x * 32 * KROW) + o_nat;
+                // the matrix-core phases run at raised wave priority: where both
+                // waves of a SIMD can issue, the one feeding the matrix core goes
+                // first and the other's vector work fills its gaps
+                prio(1);
                 bf16x8 kq[PF_KV], vq[PF_KV];
 #pragma unroll
                 for (int i = 0; i < PF_KV; ++i) {
@@ -829,6 +833,7 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
                     dpt = mfma32(va, df[c], dpt);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                prio(0);
                 float p[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, -l2q));
@@ -847,6 +852,7 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
                 bf16x8 dsf[2];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dsf[r >> 3][r & 7] = (__bf16)(p[r] * (dpt[r] - dlq));
+                prio(1);
                 // dQ^T += K^T dS^T (K^T by transposed loads of the K rows, PF_TR steps ahead)
                 const uint32_t tk = lds_off(st) + (uint32_t)(x * 32 * KROW) + o_tr;
                 bf16x8 tq[PF_TR];
@@ -861,6 +867,7 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
                     acc[db] = mfma32(ta, dsf[c2], acc[db]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                prio(0);
                 // keep the two key halves apart: interleaving them needs more
                 // registers than a wave has
                 __builtin_amdgcn_sched_barrier(0);

@@ -17,6 +17,15 @@
 
 namespace treeattn {
 
+// Wave issue priority (s_setprio 0 or 1), fenced so that the compiler keeps
+// the instructions of a phase on their side of the change.
+__device__ __forceinline__ void prio(int level) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (level) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
