@@ -11,11 +11,14 @@ namespace treeattn {
 constexpr int KT = 64;
 // Work queues of the persistent query-stationary kernels (one per XCD).
 constexpr int kItemQueues = 8;
-// Work-queue counters after the item queues: the isolated-slot unit queue and
-// the number of isolated tiles listed.  An isolated tile is kIsoSplit units.
+// Work-queue counters after the item queues: the isolated-slot unit queue,
+// the number of isolated tiles listed, and the number of KT-key tiles up to
+// the last one (over all rows) that holds a slot that is not isolated.  An
+// isolated tile is kIsoSplit units.
 constexpr int kIsoQueue = kItemQueues;
 constexpr int kIsoCount = kItemQueues + 1;
-constexpr int kQueueCounters = kItemQueues + 2;
+constexpr int kRealTiles = kItemQueues + 2;
+constexpr int kQueueCounters = kItemQueues + 3;
 constexpr int kIsoSplit = 8;
 
 // Query heads one workgroup serves (all heads sharing a KV head, up to 8).
@@ -61,7 +64,8 @@ constexpr int kVisitBudget = 320;
 
 // Smallest and largest subtree_end of every KT-key tile of each row ([B, T]),
 // and whether every slot of the tile is isolated; the isolated tiles listed
-// in iso_list, their number in qctr[kIsoCount].
+// in iso_list, their number in qctr[kIsoCount]; qctr[kRealTiles] = one past
+// the last tile of any row with a slot that is not isolated.
 // (Also zeroes the kQueueCounters work-queue counters at qctr first.)
 hipError_t launch_tile_ranges(const int32_t* se, int B, int N, int32_t* tmin, int32_t* tmax, int32_t* tiso,
                               int32_t* iso_list, int32_t* qctr, hipStream_t st);

@@ -643,7 +643,7 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
                                         float* __restrict__ delta, float* __restrict__ lse2,
                                         const int32_t* __restrict__ se, const int32_t* __restrict__ tmin,
                                         const int32_t* __restrict__ tmax, const int32_t* __restrict__ tiso, int B,
-                                        int N, int Hq, int Hkv, int T, int n_qtiles, int n_chunks, float scale_log2,
+                                        int N, int Hq, int Hkv, int T, int n_qblocks, int n_chunks, float scale_log2,
                                         float scale, __bf16* __restrict__ dq, int item, char* smem, int* list,
                                         int* list_meta) {
     constexpr int BM = 256 / HB;
@@ -667,7 +667,7 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
     const int GH = B * Hkv * n_chunks;
     const int gi = item % GH;
     const int qi = item / GH;
-    const int qtile = n_qtiles - 1 - qi;
+    const int qtile = n_qblocks - 1 - qi;
     const int chunk = gi % n_chunks;
     const int g = (gi / n_chunks) % Hkv;
     const int b = gi / (n_chunks * Hkv);
@@ -997,11 +997,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dq(const __bf16* __restrict__ q, c
         __syncthreads();
         return x;
     };
+    // Items cover the query blocks up to the end of the last 256-key tile with
+    // a slot that is not isolated (in any row): the dK/dV kernel reads delta
+    // and lse of every row such a tile reaches, padding rows after its real
+    // keys included.  The blocks after it are left to the isolated-slot units.
+    constexpr int BM = 256 / HB;
+    constexpr int TPK = kKvTile / KT;
+    const int real_keys = (qctr[kRealTiles] + TPK - 1) / TPK * kKvTile;
+    const int n_qblocks = min(n_qtiles, (real_keys + BM - 1) / BM);
+    const int n_work = n_qblocks * (n_items / n_qtiles);
     for (;;) {
         const int item = qx + NQ * claim(&qctr[qx]);
-        if (item >= n_items) break;
+        if (item >= n_work) break;
         const bool worked = dq_item<D, HB>(q, k, v, out, dout, lse, delta, lse2, se, tmin, tmax, tiso, B, N, Hq,
-                                           Hkv, T, n_qtiles, n_chunks, scale_log2, scale, dq, item, smem, list,
+                                           Hkv, T, n_qblocks, n_chunks, scale_log2, scale, dq, item, smem, list,
                                            list_meta);
         __syncthreads();  // the stages and the list are reused by the next item
         // one unit of the (HBM-bound) isolated-slot work after each item of

@@ -82,6 +82,7 @@ __global__ __launch_bounds__(1024) void iso_scan(const int32_t* __restrict__ tma
     __shared__ int s_base;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int carry = -1;  // largest subtree_end of the tiles before this step's
+    int real_end = 0;  // one past this thread's last tile that is not isolated
     for (int c0 = 0; c0 < T; c0 += 1024) {
         const int t = c0 + tid;
         int v = t < T ? tmax[(int64_t)b * T + t] : -1;
@@ -111,6 +112,7 @@ __global__ __launch_bounds__(1024) void iso_scan(const int32_t* __restrict__ tma
             int* f = tiso + (int64_t)b * T + t;
             flag = (*f && before < t * KT) ? 1 : 0;
             *f = flag;
+            if (!flag) real_end = t + 1;
         }
         // append the isolated tiles of this step: rank inside the wave by a
         // ballot, then wave offsets, one atomic per step for the base
@@ -131,6 +133,10 @@ __global__ __launch_bounds__(1024) void iso_scan(const int32_t* __restrict__ tma
         if (flag) iso_list[s_base + s_cnt[wave] + __popcll(m & ((1ull << lane) - 1ull))] = b * T + t;
         __syncthreads();
     }
+    // the tiles past the last non-isolated one of every row (the padding at
+    // the end of the rows) need no work items: their slots are isolated
+    real_end = wave_max_i32(real_end);
+    if (lane == 0 && real_end > 0) atomicMax(&qctr[kRealTiles], real_end);
 }
 
 // One unit of isolated-slot work of the forward: part `unit % kIsoSplit` of
@@ -178,7 +184,7 @@ __device__ __forceinline__ bool fwd_item(const __bf16* __restrict__ q, const __b
                                          const __bf16* __restrict__ v, const int32_t* __restrict__ se,
                                          const int32_t* __restrict__ tmin, const int32_t* __restrict__ tmax,
                                          const int32_t* __restrict__ tiso, int B, int N, int Hq, int Hkv, int T,
-                                         int n_qtiles, int n_chunks, float scale_log2, __bf16* __restrict__ out,
+                                         int n_qblocks, int n_chunks, float scale_log2, __bf16* __restrict__ out,
                                          float* __restrict__ lse, int item, char* smem, int* list, int* list_meta) {
     constexpr int BM = 256 / HB;          // positions per workgroup (8 waves x 32 rows = BM x HB)
     constexpr int NC = D / 16;            // 16-wide chunks of the head dim
@@ -199,7 +205,7 @@ __device__ __forceinline__ bool fwd_item(const __bf16* __restrict__ q, const __b
     const int GH = B * Hkv * n_chunks;
     const int gi = item % GH;
     const int qi = item / GH;
-    const int qt = n_qtiles - 1 - qi;  // deeper (later) query tiles first
+    const int qt = n_qblocks - 1 - qi;  // deeper (later) query tiles first
     const int chunk = gi % n_chunks;
     const int g = (gi / n_chunks) % Hkv;
     const int b = gi / (n_chunks * Hkv);
@@ -482,10 +488,16 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
         __syncthreads();
         return x;
     };
+    // Items cover the query blocks up to the last one with a slot that is not
+    // isolated (in any row); the blocks after it (the padding at the end of the
+    // rows) are left to the isolated-slot units.
+    constexpr int BM = 256 / HB;
+    const int n_qblocks = min(n_qtiles, (qctr[kRealTiles] * KT + BM - 1) / BM);
+    const int n_work = n_qblocks * (n_items / n_qtiles);
     for (;;) {
         const int item = qx + NQ * claim(&qctr[qx]);
-        if (item >= n_items) break;
-        const bool worked = fwd_item<D, HB>(q, k, v, se, tmin, tmax, tiso, B, N, Hq, Hkv, T, n_qtiles, n_chunks,
+        if (item >= n_work) break;
+        const bool worked = fwd_item<D, HB>(q, k, v, se, tmin, tmax, tiso, B, N, Hq, Hkv, T, n_qblocks, n_chunks,
                                             scale_log2, out, lse, item, smem, list, list_meta);
         __syncthreads();  // the stages and the list are reused by the next item
         // one unit of the (HBM-bound) isolated-slot work after each item of
