@@ -275,7 +275,7 @@ def bench_sweep(args):
     rope(k), tree_attn_fwd, tree_attn_bwd on device; layouts are on the host beforehand.
     Each layout is timed twice, alternating with the other, and reports its faster run.
     Peak memory is the device memory the layout's step allocates: its q/k/v/dout,
-    out/lse, dq/dk/dv and workspaces.  [TRL tree packing, "Claimed vs. verified"] reports
+    out/lse, dq/dk/dv and workspaces (the backward's sized to the layout's dK/dV plan).  [TRL tree packing, "Claimed vs. verified"] reports
     the same comparison (speedup and peak memory against packing ratio) for FlashAttention 3
     on another GPU.  Prints one JSON line."""
     import numpy as np
@@ -314,8 +314,9 @@ def bench_sweep(args):
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         wsf = torch.empty(max(lib.tree_attn_workspace_bytes(dt, 1, R, w.Hq, w.Hkv, w.D, False), 1), device=dev,
                           dtype=torch.uint8)
-        wsb = torch.empty(max(lib.tree_attn_workspace_bytes(dt, 1, R, w.Hq, w.Hkv, w.D, True), 1), device=dev,
-                          dtype=torch.uint8)
+        # the backward workspace this layout's dK/dV plan uses (fixed part + its partial-sum slots)
+        wsb = torch.empty(max(lib.tree_attn_bwd_workspace_bytes_for(dt, lay.subtree_end, w.Hq, w.Hkv, w.D), 1),
+                          device=dev, dtype=torch.uint8)
         scale = w.D ** -0.5
 
         def step(ev=None):
@@ -340,10 +341,12 @@ def bench_sweep(args):
         ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
         fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
         bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        ws_bytes = int(wsf.numel() + wsb.numel())
         del q, k, v, do, out, lse, dq, dk, dv, wsf, wsb, pos, se
         flops = 3.5 * 4.0 * w.D * w.Hq * pairs
         return {"row_len": R, "ancestor_pairs_per_head": pairs, "ms_per_step": round(ms, 4),
                 "rope_fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4), "peak_bytes": int(peak),
+                "workspace_bytes": ws_bytes,
                 "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
                 "raw_tok_s": round(w.raw_tokens / (ms * 1e-3), 1)}
 
