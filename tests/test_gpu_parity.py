@@ -471,6 +471,45 @@ def test_batch_rows_are_independent_and_deterministic():
             assert torch.allclose(x[0].float(), y[b].float(), atol=1e-2, rtol=0)
 
 
+def test_batch_rows_of_very_different_lengths():
+    """Two rows of 2,048 slots in one call: one holds a 120-token tree and is padding past it, the other
+    is nearly full.  The kernels give work items to query blocks up to the last tile of any row with a
+    non-isolated slot, so the short row's padding blocks are items (that return at once) in the batch
+    call and no items in its own call: both calls must give the same results, and the short row must
+    match the oracle."""
+    import torch
+
+    import prefix_tree_packed_dfs_amd as lib
+    log("case batch_of_a_short_and_a_full_row")
+    R = 2048
+    short = _random_workload(931, "bf16", Hq=8, Hkv=4, D=128, n_seqs=3, max_len=120)
+    full = _random_workload(932, "bf16", Hq=8, Hkv=4, D=128, n_seqs=9, max_len=700, fork_every=64)
+    rows = []
+    for w in (short, full):
+        parent, seq_last = lib.tree_build_trie(w.sequences)
+        assert len(parent) <= R
+        rows.append(lib.tree_pack_layout(parent, seq_last, R).subtree_end)
+    log(f"  real slots per row: {[int((se != np.arange(R)).sum()) for se in rows]}")
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn(2, R, 8, 128, generator=g).to(torch.bfloat16).cuda()
+    k = torch.randn(2, R, 4, 128, generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn(2, R, 4, 128, generator=g).to(torch.bfloat16).cuda()
+    do = torch.randn(2, R, 8, 128, generator=g).to(torch.bfloat16).cuda()
+    se = torch.from_numpy(np.stack(rows).astype(np.int32)).cuda()
+    out, lse = lib.tree_attn_fwd(q, k, v, se)
+    grads = lib.tree_attn_bwd(q, k, v, se, out, lse, do)
+    for b in range(2):
+        one = [t[b:b + 1].contiguous() for t in (q, k, v, se)]
+        o1, l1 = lib.tree_attn_fwd(*one)
+        assert torch.equal(o1[0], out[b]) and torch.equal(l1[0], lse[b])
+        g1 = lib.tree_attn_bwd(*one, o1, l1, do[b:b + 1].contiguous())
+        for x, y in zip(g1, grads):
+            assert torch.isfinite(y[b].float()).all()
+            assert torch.allclose(x[0].float(), y[b].float(), atol=1e-2, rtol=0)
+    short.row_len = R  # against the oracle in its 2,048-slot row, padding included
+    _run_full(short, label="short_row_alone")
+
+
 # ---------------------------------------------------------------------------
 # isolated slots (each sees only itself): one-token sequences and padding
 # ---------------------------------------------------------------------------
