@@ -632,8 +632,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv(const __bf16* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// dQ: grid (n_qtiles * B * Hkv * n_chunks), 512 threads; same work split as
-// the forward (BM positions x HB heads per workgroup, 32 rows per wave).
+// dQ: persistent 512-thread workgroups, one per CU, taking work items (BM
+// positions x HB query heads of one KV head, 32 rows per wave) as the forward
+// does: n_qblocks x B x Hkv x n_chunks items, deepest query block first.
 // ---------------------------------------------------------------------------
 // One work item of dQ: BM positions x HB query heads of one KV head.
 template <int D, int HB>
