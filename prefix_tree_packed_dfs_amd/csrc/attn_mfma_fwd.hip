@@ -178,14 +178,40 @@ __device__ __attribute__((noinline)) void fwd_iso_unit(const __bf16* __restrict_
     }
 }
 
+// Loads this lane's Q fragments of work item `item` (rows decoded as in
+// fwd_item; rows past the end of the row are zero).
+template <int D, int HB>
+__device__ __forceinline__ void fwd_load_q(const __bf16* __restrict__ q, int B, int N, int Hq, int Hkv,
+                                           int n_qblocks, int n_chunks, int item, bf16x8 (&qf)[D / 16]) {
+    constexpr int BM = 256 / HB;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int GH = B * Hkv * n_chunks;
+    const int gi = item % GH, qi = item / GH;
+    const int chunk = gi % n_chunks, g = (gi / n_chunks) % Hkv, b = gi / (n_chunks * Hkv);
+    const int head = g * (Hq / Hkv) + chunk * HB + wave % HB;
+    const int ip = (n_qblocks - 1 - qi) * BM + (wave / HB) * 32 + (lane & 31);
+    const __bf16* src = q + (((int64_t)b * N + min(ip, N - 1)) * Hq + head) * D + (lane >> 5) * 8;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+        bf16x8 z = {};
+        qf[c] = ip < N ? *reinterpret_cast<const bf16x8*>(src + 16 * c) : z;
+    }
+}
+
 // One work item of the forward: BM positions x HB query heads of one KV head.
+// Q is loaded here unless q_ready (the previous item loaded it).  After its
+// last tile the item claims the next item of its queue and loads that item's
+// Q, so the load runs during this item's epilogue; next_item returns the
+// claimed item (-1 if none was claimed: an item of isolated slots only).
 template <int D, int HB>
 __device__ __forceinline__ bool fwd_item(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                          const __bf16* __restrict__ v, const int32_t* __restrict__ se,
                                          const int32_t* __restrict__ tmin, const int32_t* __restrict__ tmax,
                                          const int32_t* __restrict__ tiso, int B, int N, int Hq, int Hkv, int T,
                                          int n_qblocks, int n_chunks, float scale_log2, __bf16* __restrict__ out,
-                                         float* __restrict__ lse, int item, char* smem, int* list, int* list_meta) {
+                                         float* __restrict__ lse, int item, char* smem, int* list, int* list_meta,
+                                         bf16x8 (&qf)[D / 16], bool q_ready, int* qctr, int qx, int NQ, int n_work,
+                                         int* s_next, int& next_item) {
     constexpr int BM = 256 / HB;          // positions per workgroup (8 waves x 32 rows = BM x HB)
     constexpr int NC = D / 16;            // 16-wide chunks of the head dim
     constexpr int NDB = D / 32;           // 32-row blocks of the head dim
@@ -226,15 +252,7 @@ __device__ __forceinline__ bool fwd_item(const __bf16* __restrict__ q, const __b
     const int posb = i0 + (wave / HB) * 32;
     const int ip = posb + l32;  // this lane's query position
 
-    bf16x8 qf[NC];
-    {
-        const __bf16* src = q + (((int64_t)b * N + min(ip, N - 1)) * Hq + head) * D + hi * 8;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            bf16x8 z = {};
-            qf[c] = ip < N ? *reinterpret_cast<const bf16x8*>(src + 16 * c) : z;
-        }
-    }
+    if (!q_ready) fwd_load_q<D, HB>(q, B, N, Hq, Hkv, n_qblocks, n_chunks, item, qf);
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) zero(acc[db]);
@@ -435,6 +453,13 @@ __device__ __forceinline__ bool fwd_item(const __bf16* __restrict__ q, const __b
                         acc[db] = mfma32(ld_tr(r0 + tr_off[db][0], r0 + tr_off[db][1]), pf[x][c2], acc[db]);
                     }
         }
+        if (resume < 0) {
+            // the last pass: claim the next item now and load its Q, in flight during the epilogue
+            if (tid == 0) *s_next = atomicAdd(&qctr[qx], 1);
+            __syncthreads();
+            next_item = qx + NQ * s_next[0];
+            if (next_item < n_work) fwd_load_q<D, HB>(q, B, N, Hq, Hkv, n_qblocks, n_chunks, next_item, qf);
+        }
         __syncthreads();  // the list is rebuilt only after every wave is done with it
     }
 
@@ -477,7 +502,7 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
     __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];
     __shared__ int list[1024];
     __shared__ int list_meta[2];
-    __shared__ int s_item;
+    __shared__ int s_item, s_next;
     const int qx = blockIdx.x % NQ;
     const int n_units = qctr[kIsoCount] * kIsoSplit;  // isolated-slot units
     bool iso_left = n_units > 0;
@@ -494,11 +519,14 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
     constexpr int BM = 256 / HB;
     const int n_qblocks = min(n_qtiles, (qctr[kRealTiles] * KT + BM - 1) / BM);
     const int n_work = n_qblocks * (n_items / n_qtiles);
-    for (;;) {
-        const int item = qx + NQ * claim(&qctr[qx]);
-        if (item >= n_work) break;
+    bf16x8 qf[D / 16];
+    int item = qx + NQ * claim(&qctr[qx]);
+    bool q_ready = false;
+    while (item < n_work) {
+        int next_item = -1;
         const bool worked = fwd_item<D, HB>(q, k, v, se, tmin, tmax, tiso, B, N, Hq, Hkv, T, n_qblocks, n_chunks,
-                                            scale_log2, out, lse, item, smem, list, list_meta);
+                                            scale_log2, out, lse, item, smem, list, list_meta, qf, q_ready, qctr,
+                                            qx, NQ, n_work, &s_next, next_item);
         __syncthreads();  // the stages and the list are reused by the next item
         // one unit of the (HBM-bound) isolated-slot work after each item of
         // matrix work, so that it is spread over the kernel instead of
@@ -508,6 +536,9 @@ __global__ __launch_bounds__(512, 1) void fwd_main(const __bf16* __restrict__ q,
             if (u < n_units) fwd_iso_unit<D>(q, k, v, iso_list, N, Hq, Hkv, T, scale, out, lse, u);
             else iso_left = false;  // the queue is empty: no more claims
         }
+        // the item the last one claimed (its Q already loaded), else a claim now
+        q_ready = next_item >= 0;
+        item = q_ready ? next_item : qx + NQ * claim(&qctr[qx]);
     }
     while (iso_left) {  // what is left of it
         const int u = claim(&qctr[kIsoQueue]);
