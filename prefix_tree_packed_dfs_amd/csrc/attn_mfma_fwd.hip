@@ -465,10 +465,14 @@ __device__ __forceinline__ bool fwd_item(const __bf16* __restrict__ q, const __b
 
     // epilogue: O = O^T / l, lse = (m + log2 l) ln 2
     const float lt = add_xor32(l_run);
-    // rows of isolated tiles belong to the isolated-slot units
-    if (ip < N && !tiso[(int64_t)b * T + ip / KT]) {
+    // The wave's 32 rows go out through its own LDS rows (idle now, chunks
+    // swizzled as the stages' rows): each store then writes 16 contiguous
+    // bytes and a row is 16 lanes of one store.  Rows of isolated tiles belong
+    // to the isolated-slot units (the wave's rows lie in one 64-slot tile).
+    {
+        constexpr int ROWB = D * 2, CH = D / 8;
+        char* stg = smem + wave * 32 * ROWB;
         const float inv = 1.f / lt;
-        __bf16* o = out + (((int64_t)b * N + ip) * Hq + head) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -476,9 +480,19 @@ __device__ __forceinline__ bool fwd_item(const __bf16* __restrict__ q, const __b
                 bf16x4 v4;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[db][grp * 4 + e] * inv);
-                *reinterpret_cast<bf16x4*>(o + db * 32 + grp * 8 + hi * 4) = v4;
+                *reinterpret_cast<bf16x4*>(stg + l32 * ROWB + (((db * 4 + grp) ^ row_swizzle<D>(l32)) * 16) +
+                                           hi * 8) = v4;
             }
-        if (hi == 0) lse[((int64_t)b * Hq + head) * N + ip] = (m_run + __log2f(lt)) * kLn2;
+        if (posb < N && !tiso[(int64_t)b * T + posb / KT]) {
+            __bf16* o = out + (((int64_t)b * N + posb) * Hq + head) * D;
+#pragma unroll
+            for (int kk = 0; kk < 32 * CH / 64; ++kk) {
+                const int e = kk * 64 + lane, r = e / CH, c = e % CH;
+                const bf16x8 val = *reinterpret_cast<const bf16x8*>(stg + r * ROWB + ((c ^ row_swizzle<D>(r)) * 16));
+                if (posb + r < N) *reinterpret_cast<bf16x8*>(o + (int64_t)r * Hq * D + c * 8) = val;
+            }
+            if (hi == 0 && ip < N) lse[((int64_t)b * Hq + head) * N + ip] = (m_run + __log2f(lt)) * kLn2;
+        }
     }
     return true;
 }
