@@ -685,18 +685,45 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
     // Q and dout of this lane's query in registers (lane halves hold the two
     // halves of each 16-wide chunk of the head dim); delta = dout . out of the
     // query is a dot over both halves, and it and lse * log2(e) are stored
-    // for the dK/dV kernel, which runs after this one.
+    // for the dK/dV kernel, which runs after this one.  (The out rows are
+    // read per lane: the stages hold the Q and dout rows of every wave only.)
     bf16x8 qf[NC], df[NC];
     float l2q, dlq;
     {
+        // The wave's Q and dout rows arrive by DMA in whole rows (16 lanes per
+        // 256-byte row, chunks swizzled as the stages' rows) into its part of
+        // the idle stages; the fragments are then LDS reads.  Every wave is
+        // past them at the tile-list barrier, before any tile overwrites them.
+        constexpr int ROWB = D * 2, CH = D / 8, RPI = 64 / CH;
+        const int p0 = i0 + (wave / HB) * 32;
+        const int pr = min(p0, N - 1);   // base row in bounds; rows past the end repeat the last one
+        const int lim = N - 1 - pr;
+        char* sq = smem + wave * 2 * 32 * ROWB;
+        const __bf16* qb = q + (((int64_t)b * N + pr) * Hq + head) * D;
+        const __bf16* dob = dout + (((int64_t)b * N + pr) * Hq + head) * D;
+#pragma unroll
+        for (int u = 0; u < 32 * ROWB / 1024; ++u) {
+            const int r = u * RPI + lane / CH;
+            const uint32_t o = (uint32_t)(min(r, lim) * Hq * D * 2 + ((lane % CH) ^ row_swizzle<D>(r)) * 16);
+            dma16s(qb, o, sq + u * 1024);
+            dma16s(dob, o, sq + 32 * ROWB + u * 1024);
+        }
         const int pc = min(ip, N - 1);
         const int64_t off = (((int64_t)b * N + pc) * Hq + head) * D + hi * 8;
+        bf16x8 ofr[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) ofr[c] = ld16<bf16x8>(out + off + 16 * c);
+        wait_vmcnt<0>();
+        const uint32_t qa = lds_off(sq) + (uint32_t)(l32 * ROWB + ((hi ^ row_swizzle<D>(l32)) * 16));
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            qf[c] = lds_ld16(qa ^ (32u * c));
+            df[c] = lds_ld16((qa ^ (32u * c)) + 32 * ROWB);
+        }
         float dot = 0.f;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            qf[c] = ld16<bf16x8>(q + off + 16 * c);
-            df[c] = ld16<bf16x8>(dout + off + 16 * c);
-            const bf16x8 of = ld16<bf16x8>(out + off + 16 * c);
+            const bf16x8 of = ofr[c];
             const bf16x8 d8 = df[c];
             dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(of, of, 0, 1),
                                                   __builtin_shufflevector(d8, d8, 0, 1), dot, false);
