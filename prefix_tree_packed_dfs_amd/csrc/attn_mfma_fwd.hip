@@ -365,8 +365,16 @@ __device__ __forceinline__ bool fwd_item(const __bf16* __restrict__ q, const __b
             for (int c = 0; c < NC; ++c)
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
-                    const int row = x * 32 + l32;
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + row * KROW + ((32 * c) ^ nat_x));
+                    bf16x8 a;
+                    // Up to two heads per item: one base register per lane, the chunk XORed in and the
+                    // row block as an immediate offset. At four and eight heads (more live registers)
+                    // per-load offsets measured faster.
+                    if constexpr (HB <= 2) {
+                        a = lds_ld16(((lds_off(st) + (uint32_t)(l32 * KROW + nat_x)) ^ (32u * c)) +
+                                     (uint32_t)(x * 32 * KROW));
+                    } else {
+                        a = *reinterpret_cast<const bf16x8*>(st + (x * 32 + l32) * KROW + ((32 * c) ^ nat_x));
+                    }
                     sacc[x] = c == 0 ? mfma32(a, qf[c], f32x16{}) : mfma32(a, qf[c], sacc[x]);
                 }
         };
@@ -449,8 +457,15 @@ __device__ __forceinline__ bool fwd_item(const __bf16* __restrict__ q, const __b
                 for (int x = 0; x < 2; ++x)
 #pragma unroll
                     for (int c2 = 0; c2 < 2; ++c2) {
-                        const char* r0 = st + KBYTES + (x * 32 + c2 * 16) * KROW;
-                        acc[db] = mfma32(ld_tr(r0 + tr_off[db][0], r0 + tr_off[db][1]), pf[x][c2], acc[db]);
+                        bf16x8 a;
+                        if constexpr (HB <= 2) {  // same split as for the K fragments above
+                            a = lds_tr_block<D>(lds_off(st) + (uint32_t)(KBYTES + x * 32 * KROW) + tr_offset0<D>(lane),
+                                                db, 16 * c2);
+                        } else {
+                            const char* r0 = st + KBYTES + (x * 32 + c2 * 16) * KROW;
+                            a = ld_tr(r0 + tr_off[db][0], r0 + tr_off[db][1]);
+                        }
+                        acc[db] = mfma32(a, pf[x][c2], acc[db]);
                     }
         }
         if (resume < 0) {
