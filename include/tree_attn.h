@@ -40,6 +40,11 @@
  *       lse              : [B, Hq, N] fp32, natural log
  *       subtree_end, pos_ids : [B, N] int32
  *     Query head h reads KV head h / (Hq / Hkv).  D is 64 or 128.
+ *   - Buffer sizes cannot be checked through plain pointers: each device
+ *     buffer must hold its shape above in the element type `dt` names
+ *     (lse and the index rows keep theirs).  A dtype code that does not
+ *     match the buffers (TREE_F32 for bf16 tensors, say) makes the kernels
+ *     read and write past the buffers' ends.
  *   - Integers are int32 for token ids, node ids and slots, int64 for CSR
  *     offsets into flattened arrays.
  */
