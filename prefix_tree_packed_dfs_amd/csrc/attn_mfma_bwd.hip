@@ -713,6 +713,11 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
         bf16x8 ofr[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) ofr[c] = ld16<bf16x8>(out + off + 16 * c);
+        const int64_t ro = ((int64_t)b * Hq + head) * N + pc;
+        const float lsev = lse[ro];
+        // every load of the item's start lands at this one wait, so none is
+        // left for the compiler to wait on inside the tile loop (where it
+        // would drain the prefetches of later tiles)
         wait_vmcnt<0>();
         const uint32_t qa = lds_off(sq) + (uint32_t)(l32 * ROWB + ((hi ^ row_swizzle<D>(l32)) * 16));
 #pragma unroll
@@ -734,18 +739,13 @@ __device__ __forceinline__ bool dq_item(const __bf16* __restrict__ q, const __bf
             dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(of, of, 6, 7),
                                                   __builtin_shufflevector(d8, d8, 6, 7), dot, false);
         }
-        const int64_t ro = ((int64_t)b * Hq + head) * N + pc;
-        l2q = lse[ro] * kLog2e;
+        l2q = lsev * kLog2e;
         dlq = add_xor32(dot);
         if (ip < N && hi == 0) {
             delta[ro] = dlq;
             lse2[ro] = l2q;
         }
     }
-    // these loads complete before any prefetch is issued, so the compiler's
-    // wait for them is not placed inside the tile loop (where it would drain
-    // the prefetches of later tiles)
-    wait_vmcnt<0>();
     {
         // a block of isolated slots only: its gradients are written by the
         // isolated-slot units
