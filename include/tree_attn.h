@@ -33,8 +33,10 @@
  *   - The caller owns and allocates every buffer.  Host entry points take
  *     host pointers; device entry points take device pointers and enqueue
  *     asynchronously on `stream` (a hipStream_t; NULL = the default stream).
- *     The library keeps no state between calls (beyond a per-device count of
- *     compute units, read once) and is thread-safe.
+ *     The library keeps no state between calls beyond a per-device count of
+ *     compute units (read once) and the per-device scratch array of
+ *     tree_attn_fwd_noalloc (below), and is thread-safe (that one entry
+ *     point excepted, as it says).
  *   - Device tensors are contiguous:
  *       q, out, dout, dq : [B, N, Hq, D]      k, v, dk, dv : [B, N, Hkv, D]
  *       lse              : [B, Hq, N] fp32, natural log
