@@ -134,10 +134,11 @@ def tile_classes(w, se, R):
 
 def algorithmic_bytes(w, n):
     """What the path must move per call (bf16 / fp32 elements, fp32 lse and delta): forward reads q, k, v
-    and writes out, lse; backward reads q, k, v, out, dout, lse, reads and writes delta, writes dq, dk, dv."""
+    and writes out, lse; backward reads q, k, v, out, dout and lse (4 bytes a row), writes and reads delta
+    (8), and writes dq, dk, dv."""
     e = 2 if w.dtype == "bf16" else 4
     fwd = n * ((w.Hq + 2 * w.Hkv) * w.D * e + w.Hq * w.D * e + 4 * w.Hq)
-    bwd = n * (2 * (w.Hq + 2 * w.Hkv) * w.D * e + 2 * w.Hq * w.D * e + 8 * w.Hq)
+    bwd = n * (2 * (w.Hq + 2 * w.Hkv) * w.D * e + 2 * w.Hq * w.D * e + 12 * w.Hq)
     return fwd, bwd
 
 
