@@ -161,7 +161,8 @@ def cpu_baseline(w, total_flops, target_s):
     from synth import feature_tables
 
     tables = feature_tables(w)
-    # grow the sample until one run takes about target_s / 4, then time it
+    # grow the sample until one fwd + bwd run takes at least target_s / 2 (10 s by default; the
+    # growth runs and the forward-only run bring the leg to about 1.5 x target_s)
     k = 1
     raw_all = w.raw_tokens
     while True:
@@ -169,9 +170,9 @@ def cpu_baseline(w, total_flops, target_s):
         t0 = time.perf_counter()
         tree_attention(seqs, w.fid[:k], w.dkey[:k], tables, theta=w.theta, backward=True, storage=w.dtype)
         dt = time.perf_counter() - t0
-        if dt > target_s / 4 or k == len(w.sequences):
+        if dt >= target_s / 2 or k == len(w.sequences):
             break
-        k = min(len(w.sequences), max(k + 1, int(k * (target_s / 4) / max(dt, 1e-3))))
+        k = min(len(w.sequences), max(k + 1, int(k * (target_s / 2) / max(dt, 1e-3)) + 1))
     raw_k = sum(len(s) for s in seqs)
     t0 = time.perf_counter()
     tree_attention(seqs, w.fid[:k], w.dkey[:k], tables, theta=w.theta, backward=False, storage=w.dtype)
